@@ -1,0 +1,20 @@
+"""CPU fp64 oracle (test infrastructure only; see reference.py's header)."""
+
+from .reference import (  # noqa: F401
+    to_f64,
+    attention,
+    merge,
+    merge_many,
+    updated_positions,
+    update_count,
+    gate_count,
+    head_cosine,
+    gate_cosine,
+    varlen_pack,
+    step_gates,
+    refresh_steps,
+    prefix_rows,
+    block_rows,
+    run_block,
+    run_varlen,
+)
