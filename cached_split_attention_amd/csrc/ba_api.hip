@@ -1,0 +1,391 @@
+// C-ABI front end: argument validation, launch planning and dispatch.
+// Every check happens before the first launch, so a non-OK status means
+// nothing was enqueued.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "ba_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ba_status fail(ba_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ba_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BA_OK;
+  return fail(BA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int esize_of(int dtype) { return dtype == BA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Resolved shape of one attention request.
+struct AttnShape {
+  int group;
+  bool varlen;
+  float scale;
+};
+
+ba_status check_desc(const ba_attn_desc* d, AttnShape* out) {
+  if (!d) return fail(BA_ERR_NULL, "descriptor is NULL");
+  if (d->dtype != BA_BF16 && d->dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->n_seq < 0 || d->max_q < 0 || d->max_k < 0)
+    return fail(BA_ERR_SHAPE, "negative size (n_seq %d, max_q %d, max_k %d)", d->n_seq, d->max_q, d->max_k);
+  if (d->hq < 1 || d->hkv < 1) return fail(BA_ERR_SHAPE, "hq %d and hkv %d must be >= 1", d->hq, d->hkv);
+  if (d->hq % d->hkv) return fail(BA_ERR_SHAPE, "hq %d is not a multiple of hkv %d", d->hq, d->hkv);
+  if (d->d != 64 && d->d != 128) return fail(BA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if ((d->cu_q == nullptr) != (d->cu_k == nullptr))
+    return fail(BA_ERR_SHAPE, "cu_q and cu_k must both be set (varlen) or both be NULL (dense)");
+  const bool varlen = d->cu_q != nullptr;
+  const bool has_rows = d->n_seq > 0 && d->max_q > 0;
+  if (has_rows && !d->q) return fail(BA_ERR_NULL, "q is NULL");
+  if (has_rows && d->max_k > 0 && (!d->k || !d->v)) return fail(BA_ERR_NULL, "k or v is NULL");
+  const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
+  const char* nm[3] = {"q", "k", "v"};
+  const int es = esize_of(d->dtype);
+  for (int t = 0; t < 3; ++t) {
+    for (int a = 0; a < 3; ++a)
+      if (st[t][a] < 0) return fail(BA_ERR_SHAPE, "%s_stride[%d] = %lld is negative", nm[t], a, (long long)st[t][a]);
+    for (int a = varlen ? 1 : 0; a < 3; ++a)
+      if ((st[t][a] * es) % 16)
+        return fail(BA_ERR_UNSUPPORTED, "%s_stride[%d] = %lld elements is not a multiple of 16 bytes", nm[t], a,
+                    (long long)st[t][a]);
+  }
+  if ((d->q && !aligned16(d->q)) || (d->k && !aligned16(d->k)) || (d->v && !aligned16(d->v)))
+    return fail(BA_ERR_UNSUPPORTED, "q, k and v must be 16-byte aligned");
+  if ((int64_t)d->n_seq * d->hkv > 65535 && !varlen)
+    return fail(BA_ERR_UNSUPPORTED, "n_seq * hkv = %lld exceeds 65535", (long long)d->n_seq * d->hkv);
+  if ((int64_t)d->n_seq * d->hkv > 65535) return fail(BA_ERR_UNSUPPORTED, "n_seq * hkv exceeds 65535");
+  out->group = d->hq / d->hkv;
+  out->varlen = varlen;
+  out->scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)d->d);
+  return BA_OK;
+}
+
+// Split-KV plan for prefix attention.
+struct PrefixPlan {
+  ba::Bf16Plan bf;
+  int row_tiles;
+  int n_splits;
+  int chunk;
+};
+
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
+  PrefixPlan pp{};
+  if (d->dtype == BA_F32) {
+    pp.row_tiles = 1;
+    pp.n_splits = 1;
+    pp.chunk = d->max_k > 0 ? d->max_k : 1;
+    return pp;
+  }
+  const int rows = group * d->max_q;
+  pp.bf = ba::plan_bf16(d->d, rows, d->max_k, true);
+  pp.row_tiles = (rows + pp.bf.rows_per_wg - 1) / pp.bf.rows_per_wg;
+  if (pp.row_tiles < 1) pp.row_tiles = 1;
+  const int64_t items = (int64_t)d->n_seq * d->hkv * pp.row_tiles;
+  const int kpi = pp.bf.keys_per_iter;
+  const int64_t iters = (d->max_k + kpi - 1) / kpi;
+  // Aim for about two workgroups per compute unit (256 CUs), each streaming
+  // at least two iteration tiles.
+  const int64_t target = 512;
+  int64_t splits = items > 0 ? (target + items - 1) / items : 1;
+  const int64_t max_splits = iters / 2 > 1 ? iters / 2 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t chunk_iters = (iters + splits - 1) / splits;
+  if (chunk_iters < 1) chunk_iters = 1;
+  pp.chunk = (int)(chunk_iters * kpi);
+  pp.n_splits = d->max_k > 0 ? (int)((d->max_k + pp.chunk - 1) / pp.chunk) : 1;
+  if (pp.n_splits < 1) pp.n_splits = 1;
+  return pp;
+}
+
+size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
+  if (pp.n_splits <= 1) return 0;
+  const size_t entries = (size_t)d->n_seq * d->max_q * d->hq;
+  return (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float) + 256;
+}
+
+ba::AttnParams base_params(const ba_attn_desc* d, const AttnShape& sh) {
+  ba::AttnParams p{};
+  p.q = d->q;
+  p.k = d->k;
+  p.v = d->v;
+  p.qs0 = d->q_stride[0];
+  p.qs1 = d->q_stride[1];
+  p.qs2 = d->q_stride[2];
+  p.ks0 = d->k_stride[0];
+  p.ks1 = d->k_stride[1];
+  p.ks2 = d->k_stride[2];
+  p.vs0 = d->v_stride[0];
+  p.vs1 = d->v_stride[1];
+  p.vs2 = d->v_stride[2];
+  p.cu_q = d->cu_q;
+  p.cu_k = d->cu_k;
+  p.n_seq = d->n_seq;
+  p.hq = d->hq;
+  p.hkv = d->hkv;
+  p.group = sh.group;
+  p.max_q = d->max_q;
+  p.max_k = d->max_k;
+  p.scale_log2 = sh.scale * 1.44269504088896340736f;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ba_last_error(void) { return g_err.c_str(); }
+
+int32_t ba_version(void) { return (1 << 16) | 0; }
+
+size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
+  AttnShape sh;
+  if (check_desc(desc, &sh) != BA_OK) return 0;
+  return prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
+}
+
+ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  AttnShape sh;
+  ba_status st = check_desc(desc, &sh);
+  if (st != BA_OK) return st;
+  if (desc->n_seq == 0 || desc->max_q == 0) return BA_OK;
+  if (!a_out || !l_out) return fail(BA_ERR_NULL, "a_out and l_out are required");
+  const PrefixPlan pp = plan_prefix(desc, sh.group);
+  const size_t need = prefix_ws_bytes(desc, pp);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (pp.row_tiles > 65535) return fail(BA_ERR_UNSUPPORTED, "too many query rows per KV head");
+  ba::AttnParams p = base_params(desc, sh);
+  p.decision = desc->decision;
+  p.chunk = pp.chunk;
+  p.n_splits = pp.n_splits;
+  p.row_tiles = pp.row_tiles;
+  if (desc->dtype == BA_F32) {
+    p.mode = ba::kPrefixFinal;
+    p.a = a_out;
+    p.l = l_out;
+    return hip_status(ba::launch_attn_f32(p, desc->d, stream), "prefix attention (f32)");
+  }
+  if (pp.n_splits == 1) {
+    p.mode = ba::kPrefixFinal;
+    p.a = a_out;
+    p.l = l_out;
+    return hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention");
+  }
+  const size_t entries = (size_t)desc->n_seq * desc->max_q * desc->hq;
+  p.mode = ba::kPrefixPartial;
+  p.ws_a = static_cast<float*>(workspace);
+  p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
+  st = hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention (split)");
+  if (st != BA_OK) return st;
+  ba::CombineParams c{};
+  c.ws_a = p.ws_a;
+  c.ws_l = p.ws_l;
+  c.a = a_out;
+  c.l = l_out;
+  c.cu_q = desc->cu_q;
+  c.cu_k = desc->cu_k;
+  c.decision = desc->decision;
+  c.n_seq = desc->n_seq;
+  c.hq = desc->hq;
+  c.max_q = desc->max_q;
+  c.max_k = desc->max_k;
+  c.chunk = pp.chunk;
+  c.n_splits = pp.n_splits;
+  c.d = desc->d;
+  return hip_status(ba::launch_combine(c, stream), "split-KV combine");
+}
+
+ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache, float* a_in,
+                        float* l_in, float* a_full, float* l_full, hipStream_t stream) {
+  g_err.clear();
+  AttnShape sh;
+  ba_status st = check_desc(desc, &sh);
+  if (st != BA_OK) return st;
+  if ((a_cache == nullptr) != (l_cache == nullptr))
+    return fail(BA_ERR_NULL, "a_cache and l_cache must both be given or both be NULL");
+  if ((a_full || l_full) && !a_cache) return fail(BA_ERR_NULL, "a_full / l_full need the cache to merge with");
+  if (!a_in && !l_in && !a_full && !l_full) return fail(BA_ERR_NULL, "no output given");
+  if (desc->n_seq == 0 || desc->max_q == 0) return BA_OK;
+  ba::AttnParams p = base_params(desc, sh);
+  p.decision = nullptr;
+  p.mode = ba::kBlock;
+  p.chunk = desc->max_k > 0 ? desc->max_k : 1;
+  p.n_splits = 1;
+  p.a = a_in;
+  p.l = l_in;
+  p.a_cache = a_cache;
+  p.l_cache = l_cache;
+  p.a_full = a_full;
+  p.l_full = l_full;
+  if (desc->dtype == BA_F32) return hip_status(ba::launch_attn_f32(p, desc->d, stream), "block attention (f32)");
+  const int rows = sh.group * desc->max_q;
+  const ba::Bf16Plan bf = ba::plan_bf16(desc->d, rows, desc->max_k, false);
+  p.row_tiles = (rows + bf.rows_per_wg - 1) / bf.rows_per_wg;
+  if (p.row_tiles > 65535) return fail(BA_ERR_UNSUPPORTED, "too many query rows per KV head");
+  return hip_status(ba::launch_attn_bf16(bf, p, desc->d, stream), "block attention");
+}
+
+ba_status ba_lse_merge(int64_t rows, int32_t d, const float* a1, const float* l1, const float* a2,
+                       const float* l2, float* a, float* l, hipStream_t stream) {
+  g_err.clear();
+  if (rows < 0) return fail(BA_ERR_SHAPE, "rows %lld is negative", (long long)rows);
+  if (d < 4 || d > 1024 || d % 4) return fail(BA_ERR_UNSUPPORTED, "d %d (must be a multiple of 4 in [4, 1024])", d);
+  if (rows == 0) return BA_OK;
+  if (!a1 || !l1 || !a2 || !l2 || !a) return fail(BA_ERR_NULL, "a1, l1, a2, l2 and a are required");
+  if (!aligned16(a1) || !aligned16(a2) || !aligned16(a))
+    return fail(BA_ERR_UNSUPPORTED, "a1, a2 and a must be 16-byte aligned");
+  if ((rows + (256 / (d / 4)) - 1) / (256 / (d / 4)) > 0x7fffffffLL) return fail(BA_ERR_SHAPE, "too many rows");
+  ba::MergeParams p{rows, d, a1, l1, a2, l2, a, l};
+  return hip_status(ba::launch_merge(p, stream), "lse merge");
+}
+
+size_t ba_reuse_gate_workspace(const ba_gate_desc* g) {
+  if (!g || g->n_seq < 0 || g->hq < 1 || g->n_blk < 1 || g->d < 1) return 0;
+  return ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
+}
+
+ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, uint8_t* decision, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!g) return fail(BA_ERR_NULL, "gate descriptor is NULL");
+  if (g->mode != BA_GATE_COUNT && g->mode != BA_GATE_COSINE) return fail(BA_ERR_SHAPE, "unknown gate mode %d", g->mode);
+  if (g->dtype != BA_BF16 && g->dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", g->dtype);
+  if (g->n_seq < 0 || g->n_blk < 1 || g->hq < 1 || g->d < 1)
+    return fail(BA_ERR_SHAPE, "sizes n_seq %d, n_blk %d, hq %d, d %d", g->n_seq, g->n_blk, g->hq, g->d);
+  if (g->n_seq > 65535 || g->n_blk > 0x7fffffff / 2) return fail(BA_ERR_UNSUPPORTED, "too many sequences");
+  if (!decision) return fail(BA_ERR_NULL, "decision is required");
+  const bool count = g->mode == BA_GATE_COUNT;
+  if (count && !m_count) return fail(BA_ERR_NULL, "m_count is required in count mode");
+  if (count && !g->upd_mask) {
+    if (!g->q_cur || !g->q_prev) return fail(BA_ERR_NULL, "q_cur and q_prev are required");
+    if ((g->k_cur == nullptr) != (g->k_prev == nullptr) || (g->v_cur == nullptr) != (g->v_prev == nullptr))
+      return fail(BA_ERR_NULL, "k_cur/k_prev and v_cur/v_prev must be given in pairs");
+    if ((g->k_cur || g->v_cur) && (g->hkv < 1 || g->hq % g->hkv))
+      return fail(BA_ERR_SHAPE, "hkv %d must divide hq %d", g->hkv, g->hq);
+  }
+  if (!count) {
+    if (!g->q_cur || !g->q_prev) return fail(BA_ERR_NULL, "q_cur and q_prev are required");
+    if (g->hq > 65535) return fail(BA_ERR_UNSUPPORTED, "hq > 65535");
+  }
+  for (int a = 0; a < 3; ++a)
+    if (g->q_stride[a] < 0 || g->kv_stride[a] < 0) return fail(BA_ERR_SHAPE, "negative stride");
+  const size_t need = ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
+  if (!workspace || workspace_bytes < need)
+    return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (g->n_seq == 0) return BA_OK;
+  ba::GateParams p{};
+  p.mode = g->mode;
+  p.esize = esize_of(g->dtype);
+  p.n_seq = g->n_seq;
+  p.n_blk = g->n_blk;
+  p.hq = g->hq;
+  p.hkv = g->hkv;
+  p.d = g->d;
+  p.q_cur = g->q_cur;
+  p.q_prev = g->q_prev;
+  p.qs0 = g->q_stride[0];
+  p.qs1 = g->q_stride[1];
+  p.qs2 = g->q_stride[2];
+  p.k_cur = g->k_cur;
+  p.k_prev = g->k_prev;
+  p.v_cur = g->v_cur;
+  p.v_prev = g->v_prev;
+  p.ks0 = g->kv_stride[0];
+  p.ks1 = g->kv_stride[1];
+  p.ks2 = g->kv_stride[2];
+  p.upd_mask = count ? g->upd_mask : nullptr;
+  p.tau = g->tau;
+  p.gamma = g->gamma;
+  p.cache_valid = g->cache_valid ? 1 : 0;
+  p.chunks = count ? 1 : ba::gate_cos_chunks(g->n_blk, g->d);
+  bool v16 = (g->d * p.esize) % 16 == 0;
+  const void* ptrs[6] = {g->q_cur, g->q_prev, g->k_cur, g->k_prev, g->v_cur, g->v_prev};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) v16 = false;
+  for (int a = 0; a < 3; ++a) {
+    if ((g->q_stride[a] * p.esize) % 16) v16 = false;
+    if ((g->k_cur || g->v_cur) && (g->kv_stride[a] * p.esize) % 16) v16 = false;
+  }
+  p.vec16 = v16 ? 1 : 0;
+  p.m_count = count ? m_count : nullptr;
+  p.cos = count ? nullptr : cos;
+  p.decision = decision;
+  p.ws_int = static_cast<int32_t*>(workspace);
+  const size_t nbh = (size_t)g->n_seq * g->hq;
+  p.ws_dbl = reinterpret_cast<double*>(static_cast<char*>(workspace) + ((nbh * sizeof(int32_t) + 15) & ~(size_t)15));
+  return hip_status(ba::launch_gate(p, stream), "reuse gate");
+}
+
+ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host, const uint8_t* locked,
+                         int32_t* cu_seqlens_q, int32_t* gather_idx, int32_t* total, int32_t dtype, int32_t h,
+                         int32_t d, const void* q_src, const int64_t q_src_stride[2], void* q_packed,
+                         hipStream_t stream) {
+  g_err.clear();
+  if (n_branch < 0 || n_branch > ba::kMaxBranches)
+    return fail(BA_ERR_SHAPE, "n_branch %d out of [0, %d]", n_branch, ba::kMaxBranches);
+  if (n_branch > 0 && !block_sizes_host) return fail(BA_ERR_NULL, "block_sizes_host is NULL");
+  if (!cu_seqlens_q || !total) return fail(BA_ERR_NULL, "cu_seqlens_q and total are required");
+  int32_t starts[ba::kMaxBranches + 1];
+  int64_t run = 0;
+  starts[0] = 0;
+  for (int b = 0; b < n_branch; ++b) {
+    if (block_sizes_host[b] < 0) return fail(BA_ERR_SHAPE, "block_sizes_host[%d] = %d is negative", b, block_sizes_host[b]);
+    run += block_sizes_host[b];
+    if (run > 0x7fffffff) return fail(BA_ERR_SHAPE, "total block size overflows int32");
+    starts[b + 1] = (int32_t)run;
+  }
+  const int n_total = (int)run;
+  if (n_total > 0 && (!locked || !gather_idx)) return fail(BA_ERR_NULL, "locked and gather_idx are required");
+  if ((q_src == nullptr) != (q_packed == nullptr))
+    return fail(BA_ERR_NULL, "q_src and q_packed must both be given or both be NULL");
+  int es = 2;
+  bool v16 = false;
+  if (q_src) {
+    if (dtype != BA_BF16 && dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (h < 1 || d < 1) return fail(BA_ERR_SHAPE, "h %d and d %d must be >= 1", h, d);
+    if (!q_src_stride) return fail(BA_ERR_NULL, "q_src_stride is NULL");
+    if (q_src_stride[0] < 0 || q_src_stride[1] < 0) return fail(BA_ERR_SHAPE, "negative stride");
+    es = esize_of(dtype);
+    if ((d * es) % 2) return fail(BA_ERR_SHAPE, "row bytes must be even");
+    v16 = (d * es) % 16 == 0 && aligned16(q_src) && aligned16(q_packed) && (q_src_stride[0] * es) % 16 == 0 &&
+          (q_src_stride[1] * es) % 16 == 0;
+  }
+  ba::PackParams p{};
+  p.n_branch = n_branch;
+  p.n_total = n_total;
+  p.locked = locked;
+  p.cu = cu_seqlens_q;
+  p.gather = gather_idx;
+  p.total = total;
+  p.esize = es;
+  p.h = h;
+  p.d = d;
+  p.q_src = q_src;
+  p.qs0 = q_src ? q_src_stride[0] : 0;
+  p.qs1 = q_src ? q_src_stride[1] : 0;
+  p.q_packed = q_packed;
+  p.vec16 = v16 ? 1 : 0;
+  return hip_status(ba::launch_pack(p, starts, stream), "varlen pack");
+}
+
+}  // extern "C"

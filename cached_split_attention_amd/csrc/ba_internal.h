@@ -1,0 +1,124 @@
+// Internal interfaces between the C-ABI front end (ba_api.hip) and the
+// kernel translation units.  Nothing here is exported.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "ba.h"
+
+namespace ba {
+
+// What an attention launch writes.
+enum AttnMode : int {
+  kPrefixFinal = 0,   // prefix attention, one split: A_out/L_out directly
+  kPrefixPartial = 1, // prefix attention, split k: partials into the workspace
+  kBlock = 2,         // in-block attention (+ optional fused merge)
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs0, qs1, qs2;
+  int64_t ks0, ks1, ks2;
+  int64_t vs0, vs1, vs2;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const uint8_t* decision;
+  int n_seq, hq, hkv, group, max_q, max_k;
+  float scale_log2;   // softmax scale * log2(e)
+  int chunk;          // keys per split
+  int n_splits;
+  int row_tiles;      // row tiles per (sequence, KV head)
+  int mode;
+  // outputs / merge inputs
+  float* a;           // A_out (prefix final) or A_in (block), may be null in block mode
+  float* l;
+  float* ws_a;        // [n_splits][n_seq*max_q][hq][d]
+  float* ws_l;        // [n_splits][n_seq*max_q][hq]
+  const float* a_cache;
+  const float* l_cache;
+  float* a_full;
+  float* l_full;
+};
+
+struct CombineParams {
+  const float* ws_a;
+  const float* ws_l;
+  float* a;
+  float* l;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const uint8_t* decision;
+  int n_seq, hq, max_q, max_k, chunk, n_splits, d;
+};
+
+// Launch-shape choice for the bf16 matrix-core kernel.
+struct Bf16Plan {
+  int variant;        // index into the instantiated kernel table
+  int rows_per_wg;    // query rows one workgroup covers
+  int keys_per_iter;  // keys one workgroup stages per iteration
+};
+
+Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix);
+hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+struct MergeParams {
+  int64_t rows;
+  int d;
+  const float* a1;
+  const float* l1;
+  const float* a2;
+  const float* l2;
+  float* a;
+  float* l;
+};
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
+struct GateParams {
+  int mode, esize;
+  int n_seq, n_blk, hq, hkv, d;
+  const void* q_cur;
+  const void* q_prev;
+  int64_t qs0, qs1, qs2;
+  const void* k_cur;
+  const void* k_prev;
+  const void* v_cur;
+  const void* v_prev;
+  int64_t ks0, ks1, ks2;
+  const uint8_t* upd_mask;
+  int tau;
+  double gamma;
+  int cache_valid;
+  int chunks;          // cosine mode: position chunks per (sequence, head)
+  int vec16;           // 1 if every row start is 16-byte aligned
+  int32_t* m_count;
+  double* cos;
+  uint8_t* decision;
+  int32_t* ws_int;     // tickets / counters
+  double* ws_dbl;      // cosine partials
+};
+int gate_cos_chunks(int n_blk, int d);
+size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d);
+hipError_t launch_gate(const GateParams& p, hipStream_t s);
+
+constexpr int kMaxBranches = 512;
+struct PackParams {
+  int n_branch;
+  int n_total;
+  const uint8_t* locked;
+  int32_t* cu;
+  int32_t* gather;
+  int32_t* total;
+  int esize, h, d;
+  const void* q_src;
+  int64_t qs0, qs1;
+  void* q_packed;
+  int vec16;   // 1 if every copied row start is 16-byte aligned
+};
+hipError_t launch_pack(const PackParams& p, const int32_t* starts_host, hipStream_t s);
+
+}  // namespace ba

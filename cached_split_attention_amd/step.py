@@ -1,0 +1,82 @@
+"""One denoising step of cached split attention, as a sequence of library calls.
+
+FlashBlock (gist.science/es/paper/2602.05305), section 2: each step runs the
+reuse gate, recomputes the out-of-block part (A_out, L_out) only for the
+(sequence, head) pairs the gate sends to recompute (the kernel itself skips
+the others, reading the decision from device memory, so there is no
+device-to-host synchronisation), then computes the in-block part and merges
+it with the cache in one fused kernel.  The cache stays valid until the next
+block starts.  This module only orders calls and owns buffers; it computes
+nothing itself.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_block_attn, ba_prefix_attn,
+                  ba_prefix_attn_workspace, ba_reuse_gate, ba_reuse_gate_workspace)
+
+
+class CachedBlockAttention:
+    """State for one block's denoising schedule (dense layout).
+
+    kp, kv: prefix K/V [B, Hkv, Lp, d] ("bhsd") or [B, Lp, Hkv, d] ("bshd").
+    Block tensors passed to step() are [B, Nb, H, d].
+    gate: "count" (tau on the number of updated positions) or "cosine"
+    (gamma on the per-head cosine of Q against the previous step's).
+    """
+
+    def __init__(self, kp, vp, *, nb, hq, gate="count", tau=0, gamma=0.0, scale=None,
+                 kv_layout="bhsd"):
+        self.kp, self.vp = kp, vp
+        self.kv_layout = kv_layout
+        self.B = kp.shape[0]
+        self.hq, self.nb, self.d = hq, nb, kp.shape[-1]
+        self.mode = BA_GATE_COUNT if gate == "count" else BA_GATE_COSINE
+        self.tau, self.gamma, self.scale = tau, gamma, scale
+        dev = kp.device
+        rows = self.B * nb
+        self.a_out = torch.zeros(rows, hq, self.d, device=dev, dtype=torch.float32)
+        self.l_out = torch.zeros(rows, hq, device=dev, dtype=torch.float32)
+        self.a_full = torch.empty(rows, hq, self.d, device=dev, dtype=torch.float32)
+        self.l_full = torch.empty(rows, hq, device=dev, dtype=torch.float32)
+        self.decision = torch.zeros(self.B, hq, device=dev, dtype=torch.uint8)
+        self.m_count = torch.zeros(self.B, device=dev, dtype=torch.int32)
+        self.cos = torch.zeros(self.B, hq, device=dev, dtype=torch.float64)
+        self.cache_valid = False
+        self._ws = None
+        self._gws = None
+
+    def start_block(self, kp=None, vp=None):
+        """Invalidate the cache (a new block begins; the prefix grew)."""
+        if kp is not None:
+            self.kp, self.vp = kp, vp
+            self._ws = None
+        self.cache_valid = False
+
+    def _workspaces(self, q, k, v, q_prev, k_prev, v_prev):
+        if self._ws is None:
+            n = ba_prefix_attn_workspace(q, self.kp, self.vp, kv_layout=self.kv_layout, scale=self.scale)
+            self._ws = torch.empty(max(n, 1), device=q.device, dtype=torch.uint8)
+        if self._gws is None:
+            kw = {} if self.mode == BA_GATE_COSINE else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
+            n = ba_reuse_gate_workspace(self.mode, q, q_prev, **kw)
+            self._gws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
+
+    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None):
+        """Run one step; returns (a_full, l_full) views of the output buffers."""
+        self._workspaces(q, k, v, q_prev, k_prev, v_prev)
+        if self.mode == BA_GATE_COUNT:
+            ba_reuse_gate(self.mode, q, q_prev, k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev,
+                          tau=self.tau, cache_valid=self.cache_valid, m_count=self.m_count,
+                          decision=self.decision, workspace=self._gws, stream=stream)
+        else:
+            ba_reuse_gate(self.mode, q, q_prev, gamma=self.gamma, cache_valid=self.cache_valid,
+                          cos=self.cos, decision=self.decision, workspace=self._gws, stream=stream)
+        ba_prefix_attn(q, self.kp, self.vp, self.a_out, self.l_out, self._ws, kv_layout=self.kv_layout,
+                       decision=self.decision, scale=self.scale, stream=stream)
+        ba_block_attn(q, k, v, a_cache=self.a_out, l_cache=self.l_out, a_full=self.a_full,
+                      l_full=self.l_full, scale=self.scale, stream=stream)
+        self.cache_valid = True
+        return self.a_full, self.l_full

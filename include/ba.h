@@ -1,0 +1,212 @@
+/*
+ * ba.h - cached split attention for block diffusion, MI355X (gfx950) library.
+ *
+ * The step this library computes (FlashBlock summary, gist.science/es/paper/
+ * 2602.05305, section 2 "Metodologia: FlashBlock", "Mecanismo Central"): the
+ * active block's queries attend over a static out-of-block KV prefix, giving
+ * an output A_out and its natural log-normaliser L_out = log Z_out, and over
+ * the changing in-block tokens, giving A_in and L_in.  The two are combined by
+ * the log-space merge
+ *     m = max(L_out, L_in)
+ *     A_full = (e^{L_out-m} A_out + e^{L_in-m} A_in) / (e^{L_out-m} + e^{L_in-m})
+ * and L_full = m + log(e^{L_out-m} + e^{L_in-m}).  A_out/L_out are cached
+ * across denoising steps and reused under a gate ("Estrategias de
+ * Reutilizacion Adaptativa"): reuse when the number of updated tokens is
+ * below tau, or, per head, when the head's similarity exceeds gamma.  Queries
+ * of several branches can be packed into one variable-length buffer
+ * (BlockBatch summary, gist.science/fr/paper/2605.29233, "Methodologie",
+ * "Optimisation Systeme"); locked positions issue no query but stay attended
+ * as keys (SURELOCK summary, gist.science/es/paper/2602.06412, section 2).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller unless its
+ *     name ends in _host.  The library allocates nothing, frees nothing and
+ *     never synchronises the stream: all work is enqueued on `stream`.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     non-OK status nothing was enqueued and ba_last_error() describes why.
+ *     Device-resident metadata (cu_seqlens monotone and within bounds, lock
+ *     flags in {0,1}) is the caller's contract and is not checked.
+ *   - Element strides are in elements, never bytes; the last (head_dim) axis
+ *     is always contiguous.  Row-major "[R, H, d]" means element (r, h, c) at
+ *     (r*H + h)*d + c.
+ *   - Results are bitwise reproducible: no floating-point atomics are used
+ *     and the work split is a pure function of the shapes.
+ *   - Calls are reentrant; concurrent calls on different streams that share a
+ *     workspace race.
+ */
+#ifndef BA_H
+#define BA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BA_OK = 0,
+  BA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  BA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes / strides  */
+  BA_ERR_DTYPE = 3,       /* unknown dtype                                 */
+  BA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement   */
+  BA_ERR_WORKSPACE = 5,   /* workspace missing or too small                */
+  BA_ERR_HIP = 6          /* a HIP launch reported an error                */
+} ba_status;
+
+typedef enum { BA_BF16 = 0, BA_F32 = 1 } ba_dtype;
+
+typedef enum { BA_GATE_COUNT = 0, BA_GATE_COSINE = 1 } ba_gate_mode;
+
+/*
+ * Attention descriptor shared by ba_prefix_attn and ba_block_attn.
+ *
+ * Dense mode (cu_q == NULL and cu_k == NULL): n_seq sequences, each with
+ *   max_q query rows and max_k keys.  Query row i of sequence b, head h is
+ *   q + b*q_stride[0] + i*q_stride[1] + h*q_stride[2]; key j of KV head g is
+ *   k + b*k_stride[0] + j*k_stride[1] + g*k_stride[2] (v likewise).
+ * Varlen mode (cu_q and cu_k both non-NULL, device int32[n_seq+1], each
+ *   starting at 0 and non-decreasing): sequence b owns query rows
+ *   cu_q[b] .. cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1; the row index is
+ *   used directly with stride [1] (stride [0] is ignored).  max_q / max_k
+ *   must bound every sequence's row / key count (they size the launch).
+ * Grouped-query attention: query head h reads KV head h / (hq / hkv).
+ * Output layout of every A (float32) is [R, hq, d] and of every L (float32)
+ *   [R, hq], where R = n_seq*max_q in dense mode (row b*max_q + i) and the
+ *   packed row index cu_q[b] + i in varlen mode.
+ * decision: optional device uint8[n_seq, hq] as written by ba_reuse_gate;
+ *   1 = keep the cached A_out/L_out of that (sequence, head), 0 = recompute.
+ *   NULL = recompute everything.  Only ba_prefix_attn reads it.
+ */
+typedef struct ba_attn_desc {
+  int32_t dtype;            /* ba_dtype of q, k and v                          */
+  int32_t n_seq;            /* sequences (batch) or branches                   */
+  int32_t hq, hkv;          /* query heads, KV heads; hq % hkv == 0            */
+  int32_t d;                /* head dim: 64 or 128                             */
+  int32_t max_q, max_k;     /* rows / keys per sequence (bounds in varlen)     */
+  float scale;              /* softmax scale; <= 0 selects 1/sqrt(d)           */
+  const void* q; int64_t q_stride[3];
+  const void* k; int64_t k_stride[3];
+  const void* v; int64_t v_stride[3];
+  const int32_t* cu_q;      /* device, varlen only                             */
+  const int32_t* cu_k;      /* device, varlen only                             */
+  const uint8_t* decision;  /* device, optional (prefix only)                  */
+} ba_attn_desc;
+
+/*
+ * Out-of-block (prefix) attention, FlashBlock "Mecanismo Central": for every
+ * (sequence, query head) whose decision is 0 (or all, if decision is NULL),
+ * A_out[i] = sum_j softmax_j(s q_i.k_j) v_j over the sequence's prefix keys
+ * and L_out[i] = log sum_j exp(s q_i.k_j), written in place into the caller's
+ * cache a_out [R, hq, d] / l_out [R, hq].  Entries of (sequence, head) pairs
+ * with decision 1 are left untouched (the cached values stay).  An empty
+ * prefix gives A_out = 0, L_out = -inf.
+ * The key range is split across workgroups; partial results go to
+ * `workspace`, whose size ba_prefix_attn_workspace() returns (0 means none is
+ * needed and workspace may be NULL).  The workspace needs no initialisation.
+ */
+size_t ba_prefix_attn_workspace(const ba_attn_desc* desc);
+ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * In-block attention with the fused log-space merge, FlashBlock "Mecanismo
+ * Central": every query row attends over all of its sequence's block keys
+ * with no mask (the block is bidirectional), giving A_in / L_in.  If a_cache
+ * and l_cache are both non-NULL, they are merged with A_in/L_in by the
+ * equation in this header's preamble into a_full / l_full.  Outputs are
+ * optional individually (NULL = not written) but at least one must be given;
+ * a_full / l_full require the cache.  desc->decision is ignored.
+ */
+ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache,
+                        float* a_in, float* l_in, float* a_full, float* l_full,
+                        hipStream_t stream);
+
+/*
+ * Standalone log-space merge of two partial results over disjoint key sets
+ * (FlashBlock "Mecanismo Central", the merge equation): for each of `rows`
+ * rows, a1/a2 are float32 [rows, d], l1/l2 float32 [rows]; writes a [rows, d]
+ * and, if l is non-NULL, l [rows] = m + log(e^{l1-m} + e^{l2-m}).  A side with
+ * L = -inf weighs nothing; both -inf gives A = 0, L = -inf.  In-place use
+ * (a == a1 or a == a2, l == l1 or l == l2) is allowed.
+ */
+ba_status ba_lse_merge(int64_t rows, int32_t d, const float* a1, const float* l1,
+                       const float* a2, const float* l2, float* a, float* l,
+                       hipStream_t stream);
+
+/*
+ * Reuse gate descriptor (FlashBlock "Estrategias de Reutilizacion
+ * Adaptativa").  Block tensors are [n_seq, n_blk, heads, d] addressed with
+ * the given (sequence, position, head) element strides.
+ *   BA_GATE_COUNT: M_b = number of block positions p of sequence b whose Q,
+ *     K or V row (any head, any element) differs bitwise between *_cur and
+ *     *_prev; if upd_mask (device uint8[n_seq, n_blk]) is non-NULL, M_b is
+ *     instead the number of its nonzero entries and no tensor is read.
+ *     decision[b, h] = cache_valid && M_b < tau, the same for every head.
+ *   BA_GATE_COSINE: per (b, h), the cosine of the head's whole block Q (all
+ *     n_blk*d values) against the previous step's, accumulated in float64:
+ *     cos = dot / (sqrt(|q|^2) * sqrt(|q'|^2)), a zero norm giving cos = 0
+ *     and recompute; decision[b, h] = cache_valid && cos > gamma.
+ *   Ties (M == tau, cos == gamma) recompute; cache_valid == 0 recomputes all.
+ */
+typedef struct ba_gate_desc {
+  int32_t mode;             /* ba_gate_mode                                    */
+  int32_t dtype;            /* ba_dtype of the block tensors                   */
+  int32_t n_seq, n_blk, hq, hkv, d;
+  const void* q_cur; const void* q_prev; int64_t q_stride[3];
+  const void* k_cur; const void* k_prev;        /* count mode; both or neither */
+  const void* v_cur; const void* v_prev;        /* count mode; both or neither */
+  int64_t kv_stride[3];
+  const uint8_t* upd_mask;  /* count mode, optional                            */
+  int32_t tau;
+  double gamma;
+  int32_t cache_valid;      /* 0 = no cache yet (first step of a block)        */
+} ba_gate_desc;
+
+/*
+ * Workspace for ba_reuse_gate: it must be zero-filled before its first use;
+ * every call leaves it zero-filled again when it completes.
+ */
+size_t ba_reuse_gate_workspace(const ba_gate_desc* g);
+/*
+ * Outputs: m_count int32[n_seq] (count mode; may be NULL in cosine mode),
+ * cos float64[n_seq, hq] (cosine mode, optional), decision uint8[n_seq, hq]
+ * (required; 1 = reuse).
+ */
+ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos,
+                        uint8_t* decision, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * Varlen packing of unlocked query positions across branches (BlockBatch
+ * "Optimisation Systeme"; SURELOCK "Accion de Bloqueo").  Branch b owns block
+ * positions sum(block_sizes_host[:b]) .. ; a position with locked[p] != 0
+ * issues no query.  Writes, branch-major with ascending position:
+ *   cu_seqlens_q int32[n_branch+1]: exclusive prefix sum of unlocked counts;
+ *   gather_idx int32[N] (N = sum of block sizes): packed row r -> position,
+ *     entries r >= total set to -1;
+ *   total int32[1];
+ *   q_packed [N, h, d] (contiguous, dtype of q_src): row r < total is the
+ *     q_src row gather_idx[r]; rows >= total are left untouched.
+ * q_src rows are addressed with (position, head) element strides
+ * q_src_stride[0..1].  q_src / q_packed may both be NULL to skip the gather.
+ * 0 <= n_branch <= 512.
+ */
+ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host,
+                         const uint8_t* locked, int32_t* cu_seqlens_q, int32_t* gather_idx,
+                         int32_t* total, int32_t dtype, int32_t h, int32_t d,
+                         const void* q_src, const int64_t q_src_stride[2], void* q_packed,
+                         hipStream_t stream);
+
+/* Thread-local text of the last non-OK status ("" if none). */
+const char* ba_last_error(void);
+
+/* Library ABI version: (major << 16) | minor. */
+int32_t ba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BA_H */

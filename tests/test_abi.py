@@ -1,0 +1,163 @@
+"""CPU tests of the C-ABI library: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch
+(no GPU needed: every case here fails validation, so nothing is enqueued)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ba.h")
+
+lib_mod = pytest.importorskip("cached_split_attention_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.skip("libba.so not built")
+    return lib_mod.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("ba_prefix_attn", "ba_block_attn", "ba_lse_merge", "ba_reuse_gate", "ba_varlen_pack"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in ba.h but not exported"
+        assert name in lib_mod.EXPORTS, f"{name} has no binding prototype"
+
+
+def test_version(lib):
+    assert lib.ba_version() >> 16 == 1
+
+
+FAKE = 0x10000  # a non-NULL pointer value that is never dereferenced here
+
+
+def good_desc():
+    d = lib_mod.AttnDesc()
+    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 1, 4, 2, 128, 32, 256
+    d.q = d.k = d.v = FAKE
+    for i, s in enumerate((32 * 4 * 128, 4 * 128, 128)):
+        d.q_stride[i] = s
+    for i, s in enumerate((2 * 256 * 128, 128, 256 * 128)):
+        d.k_stride[i] = s
+        d.v_stride[i] = s
+    return d
+
+
+def status_of(lib, fn, *args):
+    st = fn(*args)
+    return st, lib.ba_last_error().decode()
+
+
+@pytest.mark.parametrize("mutate,code,text", [
+    (lambda d: setattr(d, "hkv", 3), 2, "multiple"),
+    (lambda d: setattr(d, "d", 96), 4, "head dim"),
+    (lambda d: setattr(d, "dtype", 7), 3, "dtype"),
+    (lambda d: setattr(d, "max_q", -1), 2, "negative"),
+    (lambda d: setattr(d, "q", None), 1, "q is NULL"),
+    (lambda d: setattr(d, "cu_q", FAKE), 2, "cu_q and cu_k"),
+    (lambda d: d.k_stride.__setitem__(1, 100), 4, "16 bytes"),
+    (lambda d: setattr(d, "q", FAKE + 2), 4, "aligned"),
+])
+def test_prefix_validation(lib, mutate, code, text):
+    d = good_desc()
+    mutate(d)
+    st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), FAKE, FAKE, None, 0, None)
+    assert st == code and text in msg, (st, msg)
+
+
+def test_prefix_null_desc_and_outputs(lib):
+    st, msg = status_of(lib, lib.ba_prefix_attn, None, FAKE, FAKE, None, 0, None)
+    assert st == 1
+    d = good_desc()
+    st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), None, FAKE, None, 0, None)
+    assert st == 1 and "a_out" in msg
+
+
+def test_prefix_workspace_required(lib):
+    d = good_desc()
+    need = lib.ba_prefix_attn_workspace(ctypes.byref(d))
+    assert need > 0  # a 256-key prefix for 8 heads is split across workgroups
+    st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), FAKE, FAKE, FAKE, need - 1, None)
+    assert st == 5 and "workspace" in msg
+
+
+def test_prefix_empty_is_ok_without_launch(lib):
+    d = good_desc()
+    d.n_seq = 0
+    assert lib.ba_prefix_attn(ctypes.byref(d), FAKE, FAKE, None, 0, None) == 0
+
+
+def test_block_validation(lib):
+    d = good_desc()
+    st, msg = status_of(lib, lib.ba_block_attn, ctypes.byref(d), None, None, None, None, None, None, None)
+    assert st == 1 and "no output" in msg
+    st, msg = status_of(lib, lib.ba_block_attn, ctypes.byref(d), FAKE, None, None, None, FAKE, None, None)
+    assert st == 1 and "a_cache" in msg
+    st, msg = status_of(lib, lib.ba_block_attn, ctypes.byref(d), None, None, None, None, FAKE, None, None)
+    assert st == 1 and "cache" in msg
+
+
+def test_merge_validation(lib):
+    assert lib.ba_lse_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert lib.ba_lse_merge(4, 6, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 4
+    assert lib.ba_lse_merge(4, 128, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.ba_lse_merge(0, 128, None, None, None, None, None, None, None) == 0
+
+
+def good_gate():
+    g = lib_mod.GateDesc()
+    g.mode, g.dtype, g.n_seq, g.n_blk, g.hq, g.hkv, g.d = 0, 0, 2, 32, 4, 2, 128
+    g.q_cur = g.q_prev = g.k_cur = g.k_prev = g.v_cur = g.v_prev = FAKE
+    for i, s in enumerate((32 * 4 * 128, 4 * 128, 128)):
+        g.q_stride[i] = s
+    for i, s in enumerate((32 * 2 * 128, 2 * 128, 128)):
+        g.kv_stride[i] = s
+    g.tau = 4
+    return g
+
+
+def test_gate_validation(lib):
+    g = good_gate()
+    need = lib.ba_reuse_gate_workspace(ctypes.byref(g))
+    assert need == 2 * 2 * 4
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, None, FAKE, need, None)
+    assert st == 1 and "decision" in msg
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, FAKE, FAKE, need - 1, None)
+    assert st == 5
+    g.k_prev = None
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, FAKE, FAKE, need, None)
+    assert st == 1 and "pairs" in msg
+    g = good_gate()
+    g.n_blk = 0
+    assert lib.ba_reuse_gate(ctypes.byref(g), FAKE, None, FAKE, FAKE, 64, None) == 2
+    g = good_gate()
+    g.mode = 5
+    assert lib.ba_reuse_gate(ctypes.byref(g), FAKE, None, FAKE, FAKE, 64, None) == 2
+    g = good_gate()
+    g.mode = 1
+    assert lib.ba_reuse_gate_workspace(ctypes.byref(g)) > 2 * 4 * 4
+
+
+def test_pack_validation(lib):
+    sizes = (ctypes.c_int32 * 3)(4, -1, 2)
+    st, msg = status_of(lib, lib.ba_varlen_pack, 3, sizes, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None, None, None, None)
+    assert st == 2 and "negative" in msg
+    sizes = (ctypes.c_int32 * 1)(4)
+    assert lib.ba_varlen_pack(600, sizes, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None, None, None, None) == 2
+    assert lib.ba_varlen_pack(1, sizes, None, FAKE, FAKE, FAKE, 0, 0, 0, None, None, None, None) == 1
+    assert lib.ba_varlen_pack(1, sizes, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, FAKE, None, None, None) == 1

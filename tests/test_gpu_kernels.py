@@ -1,0 +1,475 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle, on seeded
+inputs small enough for the oracle yet spanning several tiles with ragged
+tails, plus the edge cases (empty prefix, empty branches, all locked, ties,
+NaN-poisoned cache, guard bands, determinism)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_block_schedule, make_varlen_batch, round_to_bf16_bits
+from tests.gpu_util import DEV, check_a, check_l, dev_bits, dev_f32, dev_in, host
+
+pytestmark = pytest.mark.gpu
+
+ba = pytest.importorskip("cached_split_attention_amd")
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def f64(x, dtype):
+    return oracle.to_f64(x, dtype)
+
+
+# ----------------------------------------------------------------------------
+# ba_lse_merge
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_lse_merge(d):
+    r = np.random.default_rng(40 + d)
+    rows = 1237
+    a1 = r.standard_normal((rows, d)).astype(np.float32)
+    a2 = r.standard_normal((rows, d)).astype(np.float32)
+    l1 = (r.standard_normal(rows) * 5).astype(np.float32)
+    l2 = (r.standard_normal(rows) * 5).astype(np.float32)
+    l1[::7] = -np.inf
+    l2[::11] = -np.inf
+    a1[::7] = 0.0
+    a2[::11] = 0.0
+    l1[3], l2[3] = 700.0, -700.0  # extreme gap
+    wa, wl = oracle.merge(a1, l1, a2, l2)
+    ga = torch.empty(rows, d, device=DEV)
+    gl = torch.empty(rows, device=DEV)
+    ba.ba_lse_merge(dev_f32(a1), dev_f32(l1), dev_f32(a2), dev_f32(l2), ga, gl)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(ga), wa, atol=2e-6, rtol=0)
+    got_l = host(gl)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(wl))
+    fin = ~np.isneginf(wl)
+    np.testing.assert_allclose(got_l[fin], wl[fin], atol=2e-5 * max(1, np.abs(wl[fin]).max() / 100), rtol=0)
+    # in place into the first operand
+    x1, y1 = dev_f32(a1), dev_f32(l1)
+    ba.ba_lse_merge(x1, y1, dev_f32(a2), dev_f32(l2), x1, y1)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(x1), wa, atol=2e-6, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# ba_reuse_gate
+# ----------------------------------------------------------------------------
+
+def _gate_count_run(s, slicer=None, use_mask=False):
+    q = [dev_in(x, s.dtype) for x in s.q]
+    k = [dev_in(x, s.dtype) for x in s.k]
+    v = [dev_in(x, s.dtype) for x in s.v]
+    if slicer is not None:
+        q, k, v = [slicer(x) for x in q], [slicer(x) for x in k], [slicer(x) for x in v]
+    ref = oracle.step_gates(s)
+    ws = torch.zeros(ba.ba_reuse_gate_workspace(ba.BA_GATE_COUNT, q[1], q[0], k_cur=k[1], k_prev=k[0],
+                                                v_cur=v[1], v_prev=v[0]), device=DEV, dtype=torch.uint8)
+    dec = torch.empty(s.B, s.hq, device=DEV, dtype=torch.uint8)
+    m = torch.empty(s.B, device=DEV, dtype=torch.int32)
+    for t in range(1, s.steps + 1):
+        if use_mask:
+            mask = torch.from_numpy(oracle.updated_positions([s.q[t], s.k[t], s.v[t]],
+                                                             [s.q[t - 1], s.k[t - 1], s.v[t - 1]])
+                                    .astype(np.uint8)).to(DEV)
+            ba.ba_reuse_gate(ba.BA_GATE_COUNT, q[t], q[t - 1], upd_mask=mask, tau=s.tau,
+                             cache_valid=t > 1, m_count=m, decision=dec, workspace=ws)
+        else:
+            ba.ba_reuse_gate(ba.BA_GATE_COUNT, q[t], q[t - 1], k_cur=k[t], k_prev=k[t - 1], v_cur=v[t],
+                             v_prev=v[t - 1], tau=s.tau, cache_valid=t > 1, m_count=m, decision=dec,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(m.cpu().numpy(), ref[t]["m"]), (t, m.cpu().numpy(), ref[t]["m"])
+        assert np.array_equal(m.cpu().numpy(), s.touched[t])
+        assert np.array_equal(dec.cpu().numpy(), ref[t]["decision"]), t
+        assert not ws.any(), "gate workspace must be zero again after the call"
+
+
+@pytest.mark.parametrize("dtype,schedule", [("bf16", "redraw"), ("bf16", "poisson"), ("f32", "unmask"),
+                                            ("bf16", "unmask")])
+def test_gate_count(dtype, schedule):
+    s = make_block_schedule(dtype=dtype, B=3, hq=6, hkv=2, d=64, lp=8, nb=24, steps=10,
+                            schedule=schedule, redraw_range=(0, 5), poisson_lam=3.0,
+                            unmask_range=(1, 3), gate="count", tau=3, seed=50)
+    _gate_count_run(s)
+
+
+def test_gate_count_unaligned_rows_and_mask():
+    # head dim 66 sliced to 64 from position 1: rows start 2 bytes off 16
+    s = make_block_schedule(dtype="bf16", B=2, hq=2, hkv=2, d=66, lp=8, nb=16, steps=6,
+                            schedule="redraw", redraw_range=(0, 3), gate="count", tau=2, seed=51)
+    # compare only elements 1..64: changes are whole-row redraws, so counts agree
+    _gate_count_run(s, slicer=lambda x: x[..., 1:65])
+    _gate_count_run(s, use_mask=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_cosine(dtype):
+    s = make_block_schedule(dtype=dtype, B=2, hq=5, hkv=5, d=64, lp=8, nb=37, steps=5, std=1.0,
+                            schedule="qnoise", sigma_range=(0.01, 0.6), gate="cosine", gamma=0.95,
+                            seed=52)
+    ref = oracle.step_gates(s)
+    q = [dev_in(x, dtype) for x in s.q]
+    ws = torch.zeros(ba.ba_reuse_gate_workspace(ba.BA_GATE_COSINE, q[1], q[0]), device=DEV, dtype=torch.uint8)
+    dec = torch.empty(s.B, s.hq, device=DEV, dtype=torch.uint8)
+    cos = torch.empty(s.B, s.hq, device=DEV, dtype=torch.float64)
+    saw = set()
+    for t in range(1, s.steps + 1):
+        ba.ba_reuse_gate(ba.BA_GATE_COSINE, q[t], q[t - 1], gamma=s.gamma, cache_valid=t > 1, cos=cos,
+                         decision=dec, workspace=ws)
+        torch.cuda.synchronize()
+        c = cos.cpu().numpy()
+        assert np.abs(c - ref[t]["cos"]).max() <= 1e-13, np.abs(c - ref[t]["cos"]).max()
+        assert np.array_equal(dec.cpu().numpy(), ref[t]["decision"]), t
+        saw |= set(dec.cpu().numpy().ravel().tolist()) if t > 1 else set()
+        assert not ws.any()
+    assert saw == {0, 1}, "schedule should exercise both decisions"
+
+
+def test_gate_cosine_exact_tie_and_zero_norm():
+    d = 64
+    q = np.zeros((1, 1, 3, d), dtype=np.float32)
+    p = np.zeros((1, 1, 3, d), dtype=np.float32)
+    q[0, 0, 0, :2] = [3, 4]
+    p[0, 0, 0, :2] = [4, 3]        # cos = 24/25 = 0.96 exactly
+    q[0, 0, 1, :2] = [1, 2]
+    p[0, 0, 1, :2] = [1, 2]        # cos = 1
+    q[0, 0, 2, :] = 0.0            # zero norm
+    p[0, 0, 2, :2] = [1, 1]
+    for dtype in ("bf16", "f32"):
+        qq = dev_bits(round_to_bf16_bits(q)) if dtype == "bf16" else dev_f32(q)
+        pp = dev_bits(round_to_bf16_bits(p)) if dtype == "bf16" else dev_f32(p)
+        ws = torch.zeros(ba.ba_reuse_gate_workspace(ba.BA_GATE_COSINE, qq, pp), device=DEV, dtype=torch.uint8)
+        dec = torch.empty(1, 3, device=DEV, dtype=torch.uint8)
+        cos = torch.empty(1, 3, device=DEV, dtype=torch.float64)
+        for gamma, want in ((0.96, [0, 1, 0]), (0.9599, [1, 1, 0]), (-5.0, [1, 1, 0])):
+            ba.ba_reuse_gate(ba.BA_GATE_COSINE, qq, pp, gamma=gamma, cache_valid=True, cos=cos, decision=dec,
+                             workspace=ws)
+            torch.cuda.synchronize()
+            assert cos.cpu().numpy()[0, 0] == 0.96
+            assert dec.cpu().numpy()[0].tolist() == want, (dtype, gamma)
+        ba.ba_reuse_gate(ba.BA_GATE_COSINE, qq, pp, gamma=0.5, cache_valid=False, cos=cos, decision=dec,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        assert not dec.cpu().numpy().any()
+
+
+# ----------------------------------------------------------------------------
+# ba_varlen_pack
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sizes,p_lock", [((4, 8, 16, 32, 64, 128), 0.3), ((3, 0, 5, 1, 0), 0.5),
+                                          ((7, 9), 1.0), ((7, 9), 0.0), ((300, 1, 70), 0.3), ((), 0.3)])
+def test_varlen_pack(sizes, p_lock):
+    r = np.random.default_rng(len(sizes) + int(10 * p_lock))
+    n = int(sum(sizes))
+    locked = (r.random(n) < p_lock).astype(np.uint8)
+    cu_w, gather_w, total_w = oracle.varlen_pack(locked, sizes)
+    h, d = 3, 128
+    q = r.standard_normal((max(n, 1), h, d)).astype(np.float32)
+    qd = dev_bits(round_to_bf16_bits(q))
+    cu = torch.full((len(sizes) + 1,), -7, device=DEV, dtype=torch.int32)
+    gather = torch.full((max(n, 1),), -7, device=DEV, dtype=torch.int32)
+    total = torch.full((1,), -7, device=DEV, dtype=torch.int32)
+    packed = torch.zeros(max(n, 1), h, d, device=DEV, dtype=torch.bfloat16)
+    ba.ba_varlen_pack(sizes, torch.from_numpy(locked).to(DEV) if n else torch.zeros(1, dtype=torch.uint8, device=DEV),
+                      cu, gather, total, qd if n else None, packed if n else None)
+    torch.cuda.synchronize()
+    assert cu.cpu().numpy().tolist() == cu_w.tolist()
+    assert int(total.item()) == total_w
+    g = gather.cpu().numpy()
+    assert g[:total_w].tolist() == gather_w.tolist()
+    if n:
+        assert np.all(g[total_w:n] == -1)
+        got = packed.view(torch.int16).cpu().numpy()[:total_w]
+        want = qd.view(torch.int16).cpu().numpy()[gather_w]
+        assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------
+# ba_prefix_attn / ba_block_attn, dense
+# ----------------------------------------------------------------------------
+
+def _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed, std=1.0):
+    s = make_block_schedule(dtype=dtype, B=B, hq=hq, hkv=hkv, d=d, lp=lp, nb=nb, steps=0, std=std,
+                            schedule="none", seed=seed)
+    return s
+
+
+def _oracle_prefix(s, t=0):
+    out_a = np.zeros((s.B, s.nb, s.hq, s.d))
+    out_l = np.zeros((s.B, s.nb, s.hq))
+    for b in range(s.B):
+        for h in range(s.hq):
+            out_a[b, :, h], out_l[b, :, h] = oracle.prefix_rows(s, t, b, h)
+    return out_a.reshape(s.B * s.nb, s.hq, s.d), out_l.reshape(s.B * s.nb, s.hq)
+
+
+def _oracle_block(s, t=0):
+    out_a = np.zeros((s.B, s.nb, s.hq, s.d))
+    out_l = np.zeros((s.B, s.nb, s.hq))
+    for b in range(s.B):
+        for h in range(s.hq):
+            out_a[b, :, h], out_l[b, :, h] = oracle.block_rows(s, t, b, h)
+    return out_a.reshape(s.B * s.nb, s.hq, s.d), out_l.reshape(s.B * s.nb, s.hq)
+
+
+DENSE_SHAPES = [
+    # (B, hq, hkv, d, lp, nb): 128-row tiles with a ragged second tile, split-KV
+    (1, 8, 2, 128, 777, 50),
+    # 64-row tiles, GQA, split-KV with a ragged last chunk
+    (2, 4, 2, 128, 1000, 20),
+    # 32-row tiles (few rows per KV head)
+    (3, 2, 2, 128, 300, 20),
+    (1, 4, 4, 128, 64, 32),     # exactly one tile, one split
+    (2, 6, 3, 64, 555, 41),     # head dim 64
+    (1, 3, 1, 64, 129, 9),      # G = 3, 27 rows
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", DENSE_SHAPES)
+def test_prefix_attn(dtype, shape):
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=hash(shape) % 1000)
+    want_a, want_l = _oracle_prefix(s)
+    q, kp, vp = dev_in(s.q[0], dtype), dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    a = torch.full((B * nb, hq, d), 777.0, device=DEV)
+    l = torch.full((B * nb, hq), 777.0, device=DEV)
+    ba.ba_prefix_attn(q, kp, vp, a, l, ws)
+    torch.cuda.synchronize()
+    check_a(host(a), want_a, "A_out")
+    check_l(host(l), want_l, "L_out")
+    # bitwise deterministic
+    a2 = torch.zeros_like(a)
+    l2 = torch.zeros_like(l)
+    ba.ba_prefix_attn(q, kp, vp, a2, l2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, a2) and torch.equal(l, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefix_attn_decision_leaves_cache_untouched(dtype):
+    B, hq, hkv, d, lp, nb = 3, 6, 2, 128, 900, 33
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=61)
+    want_a, want_l = _oracle_prefix(s)
+    r = np.random.default_rng(3)
+    dec = (r.random((B, hq)) < 0.5).astype(np.uint8)
+    dec[0, :] = 1            # a whole sequence reused
+    dec[1, :] = 0            # a whole sequence recomputed
+    q, kp, vp = dev_in(s.q[0], dtype), dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    a = torch.full((B * nb, hq, d), 123.0, device=DEV)
+    l = torch.full((B * nb, hq), -55.0, device=DEV)
+    ba.ba_prefix_attn(q, kp, vp, a, l, ws, decision=torch.from_numpy(dec).to(DEV))
+    torch.cuda.synchronize()
+    ga, gl = host(a).reshape(B, nb, hq, d), host(l).reshape(B, nb, hq)
+    wa, wl = want_a.reshape(B, nb, hq, d), want_l.reshape(B, nb, hq)
+    for b in range(B):
+        for h in range(hq):
+            if dec[b, h]:
+                assert np.all(ga[b, :, h] == 123.0) and np.all(gl[b, :, h] == -55.0)
+            else:
+                check_a(ga[b, :, h], wa[b, :, h], f"A_out b{b} h{h}")
+                check_l(gl[b, :, h], wl[b, :, h], f"L_out b{b} h{h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefix_attn_empty_prefix(dtype):
+    s = _dense_inputs(dtype, 2, 4, 2, 128, 0, 20, seed=62)
+    q = dev_in(s.q[0], dtype)
+    kp = torch.zeros(2, 2, 0, 128, device=DEV, dtype=q.dtype)
+    a = torch.full((40, 4, 128), 5.0, device=DEV)
+    l = torch.full((40, 4), 5.0, device=DEV)
+    assert ba.ba_prefix_attn_workspace(q, kp, kp) == 0
+    ba.ba_prefix_attn(q, kp, kp, a, l)
+    torch.cuda.synchronize()
+    assert torch.all(a == 0) and torch.all(torch.isneginf(l))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefix_attn_bshd_layout(dtype):
+    s = _dense_inputs(dtype, 2, 4, 2, 128, 700, 30, seed=63)
+    want_a, want_l = _oracle_prefix(s)
+    q = dev_in(s.q[0], dtype)
+    kp = dev_in(s.kp, dtype).transpose(1, 2).contiguous()  # [B, Lp, Hkv, d]
+    vp = dev_in(s.vp, dtype).transpose(1, 2).contiguous()
+    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp, kv_layout="bshd")), device=DEV,
+                     dtype=torch.uint8)
+    a = torch.empty(60, 4, 128, device=DEV)
+    l = torch.empty(60, 4, device=DEV)
+    ba.ba_prefix_attn(q, kp, vp, a, l, ws, kv_layout="bshd")
+    torch.cuda.synchronize()
+    check_a(host(a), want_a, "A_out")
+    check_l(host(l), want_l, "L_out")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", DENSE_SHAPES)
+def test_block_attn_fused_merge(dtype, shape):
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs(dtype, B, hq, hkv, d, 4, nb, seed=hash(shape) % 997)
+    want_a, want_l = _oracle_block(s)
+    r = np.random.default_rng(5)
+    rows = B * nb
+    ac = r.standard_normal((rows, hq, d)).astype(np.float32)
+    lc = (r.standard_normal((rows, hq)) * 3 + 2).astype(np.float32)
+    lc[::5, 0] = -np.inf
+    ac[::5, 0] = 0.0
+    wf, wlf = oracle.merge(ac, lc, want_a, want_l)
+    q, k, v = dev_in(s.q[0], dtype), dev_in(s.k[0], dtype), dev_in(s.v[0], dtype)
+    outs = [torch.full((rows, hq, d), 9.0, device=DEV), torch.full((rows, hq), 9.0, device=DEV),
+            torch.full((rows, hq, d), 9.0, device=DEV), torch.full((rows, hq), 9.0, device=DEV)]
+    ba.ba_block_attn(q, k, v, a_cache=dev_f32(ac), l_cache=dev_f32(lc), a_in=outs[0], l_in=outs[1],
+                     a_full=outs[2], l_full=outs[3])
+    torch.cuda.synchronize()
+    check_a(host(outs[0]), want_a, "A_in")
+    check_l(host(outs[1]), want_l, "L_in")
+    check_a(host(outs[2]), wf, "A_full")
+    check_l(host(outs[3]), wlf, "L_full")
+    # only the merged output
+    af = torch.zeros(rows, hq, d, device=DEV)
+    ba.ba_block_attn(q, k, v, a_cache=dev_f32(ac), l_cache=dev_f32(lc), a_full=af)
+    torch.cuda.synchronize()
+    assert torch.equal(af, outs[2])
+
+
+def test_block_attn_guard_bands():
+    s = _dense_inputs("bf16", 2, 4, 2, 128, 4, 37, seed=64)
+    q, k, v = dev_bits(s.q[0]), dev_bits(s.k[0]), dev_bits(s.v[0])
+    rows = 74
+    pad = 4096
+    buf = torch.full((pad + rows * 4 * 128 + pad,), 31.0, device=DEV)
+    lbuf = torch.full((pad + rows * 4 + pad,), 31.0, device=DEV)
+    a = buf[pad:pad + rows * 4 * 128].view(rows, 4, 128)
+    l = lbuf[pad:pad + rows * 4].view(rows, 4)
+    ba.ba_block_attn(q, k, v, a_in=a, l_in=l)
+    kp, vp = dev_bits(s.kp), dev_bits(s.vp)
+    ba.ba_prefix_attn(q, kp, vp, a, l)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 31.0) and torch.all(buf[pad + rows * 512:] == 31.0)
+    assert torch.all(lbuf[:pad] == 31.0) and torch.all(lbuf[pad + rows * 4:] == 31.0)
+
+
+def test_nan_poisoned_cache():
+    """Reuse really reads the cache (NaN shows up); recompute really
+    overwrites it (NaN gone)."""
+    s = make_block_schedule(dtype="bf16", B=1, hq=4, hkv=4, d=128, lp=300, nb=16, steps=2,
+                            schedule="none", gate="count", tau=4, seed=65)
+    kp, vp = dev_bits(s.kp), dev_bits(s.vp)
+    q = [dev_bits(x) for x in s.q]
+    k = [dev_bits(x) for x in s.k]
+    v = [dev_bits(x) for x in s.v]
+    attn = ba.CachedBlockAttention(kp, vp, nb=16, hq=4, gate="count", tau=4)
+    attn.step(q[1], k[1], v[1], q[0], k[0], v[0])
+    attn.a_out.fill_(float("nan"))
+    attn.l_out.fill_(float("nan"))
+    af, _ = attn.step(q[2], k[2], v[2], q[1], k[1], v[1])   # unchanged block: reuse
+    torch.cuda.synchronize()
+    assert int(attn.decision.min()) == 1
+    assert torch.isnan(af).all()
+    attn.start_block()
+    af, _ = attn.step(q[2], k[2], v[2], q[1], k[1], v[1])   # invalid cache: recompute
+    torch.cuda.synchronize()
+    assert int(attn.decision.max()) == 0
+    assert torch.isfinite(af).all()
+
+
+# ----------------------------------------------------------------------------
+# varlen
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_varlen_attention(d):
+    vb = make_varlen_batch(block_sizes=(3, 0, 5, 8, 33, 70), prefix_lens=(100, 40, 0, 70, 300, 1111),
+                           h=4, d=d, lock_p=0.3, seed=66)
+    ref = oracle.run_varlen(vb)
+    n = int(vb.block_sizes.sum())
+    nbr = vb.block_sizes.size
+    locked = torch.from_numpy(vb.locked).to(DEV)
+    cu_q = torch.empty(nbr + 1, device=DEV, dtype=torch.int32)
+    gather = torch.empty(n, device=DEV, dtype=torch.int32)
+    total = torch.empty(1, device=DEV, dtype=torch.int32)
+    qsrc = dev_bits(vb.q)
+    qp = torch.zeros(n, vb.h, d, device=DEV, dtype=torch.bfloat16)
+    ba.ba_varlen_pack(vb.block_sizes, locked, cu_q, gather, total, qsrc, qp)
+    cu_kp = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.prefix_lens)]).astype(np.int32)).to(DEV)
+    cu_kb = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.block_sizes)]).astype(np.int32)).to(DEV)
+    kp, vp = dev_bits(vb.kp), dev_bits(vb.vp)          # [H, sum L, d]
+    kb, vbk = dev_bits(vb.k), dev_bits(vb.v)           # [sum B, H, d]
+    max_q = int(vb.block_sizes.max())
+    a_out = torch.full((n, vb.h, d), 3.0, device=DEV)
+    l_out = torch.full((n, vb.h), 3.0, device=DEV)
+    kw = dict(q_layout="thd", cu_q=cu_q, max_q=max_q)
+    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(qp, kp, vp, kv_layout="htd", cu_k=cu_kp,
+                                                         max_k=int(vb.prefix_lens.max()), **kw)),
+                     device=DEV, dtype=torch.uint8)
+    ba.ba_prefix_attn(qp, kp, vp, a_out, l_out, ws, kv_layout="htd", cu_k=cu_kp,
+                      max_k=int(vb.prefix_lens.max()), **kw)
+    a_full = torch.full((n, vb.h, d), 3.0, device=DEV)
+    l_full = torch.full((n, vb.h), 3.0, device=DEV)
+    a_in = torch.full((n, vb.h, d), 3.0, device=DEV)
+    ba.ba_block_attn(qp, kb, vbk, a_cache=a_out, l_cache=l_out, a_in=a_in, a_full=a_full, l_full=l_full,
+                     kv_layout="thd", cu_k=cu_kb, max_k=int(vb.block_sizes.max()), **kw)
+    torch.cuda.synchronize()
+    tot = ref["total"]
+    assert int(total.item()) == tot
+    assert cu_q.cpu().numpy().tolist() == ref["cu_seqlens"].tolist()
+    check_a(host(a_out)[:tot], ref["a_out"], "A_out varlen")
+    check_l(host(l_out)[:tot], ref["l_out"], "L_out varlen")
+    check_a(host(a_in)[:tot], ref["a_in"], "A_in varlen")
+    check_a(host(a_full)[:tot], ref["a_full"], "A_full varlen")
+    check_l(host(l_full)[:tot], ref["l_full"], "L_full varlen")
+    # rows past the packed total are never written
+    assert torch.all(a_full[tot:] == 3.0) and torch.all(a_out[tot:] == 3.0)
+
+
+# ----------------------------------------------------------------------------
+# whole schedules through the step driver
+# ----------------------------------------------------------------------------
+
+def _run_schedule(s, check_rows=None):
+    ref = oracle.run_block(s)
+    kp, vp = dev_in(s.kp, s.dtype), dev_in(s.vp, s.dtype)
+    q = [dev_in(x, s.dtype) for x in s.q]
+    k = [dev_in(x, s.dtype) for x in s.k]
+    v = [dev_in(x, s.dtype) for x in s.v]
+    attn = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate=s.gate, tau=s.tau, gamma=s.gamma,
+                                   scale=s.scale)
+    reuse_seen = 0
+    for t in range(1, s.steps + 1):
+        af, lf = attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+        torch.cuda.synchronize()
+        dec = attn.decision.cpu().numpy()
+        assert np.array_equal(dec, ref[t]["gate"]["decision"]), t
+        reuse_seen += int(dec.sum())
+        check_a(host(af), ref[t]["a_full"], f"A_full step {t}")
+        check_l(host(lf), ref[t]["l_full"], f"L_full step {t}")
+        check_a(host(attn.a_out), ref[t]["a_out"], f"A_out cache step {t}")
+    return reuse_seen
+
+
+def test_schedule_tiny_f32():
+    """The single-layer float32 workload: 4 heads, d = 64, prefix 256, block
+    32, 8 steps redrawing 1-4 rows, tau = 4."""
+    from workloads import preset
+    s = preset("c1_tiny_f32")
+    assert _run_schedule(s) > 0
+
+
+@pytest.mark.parametrize("schedule,gate", [("redraw", "count"), ("poisson", "count"), ("qnoise", "cosine")])
+def test_schedule_bf16(schedule, gate):
+    s = make_block_schedule(dtype="bf16", B=2, hq=4, hkv=2, d=128, lp=640, nb=40, steps=6, std=1.0,
+                            schedule=schedule, redraw_range=(0, 3), poisson_lam=1.5,
+                            sigma_range=(0.01, 0.5), gate=gate, tau=3, gamma=0.95, seed=67)
+    assert _run_schedule(s) > 0
