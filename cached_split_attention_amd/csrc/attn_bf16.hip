@@ -3,30 +3,39 @@
 //
 // The computation is the split of FlashBlock (gist.science/es/paper/2602.05305,
 // section 2, "Mecanismo Central"): each part yields an output A and its
-// natural log-normaliser L = log Z; the parts are combined by the log-space
-// merge equation of the same section.
+// natural log-normaliser L = log Z; parts are combined by the log-space merge
+// equation of the same section (also used here to combine key splits).
 //
 // Per wave (64 lanes, 32 query rows):
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K tile (32 keys x 16 dims),
-//                 B = Q^T (16 dims x 32 rows).  Lane l owns query row l%32;
-//                 its 16 accumulator values per 32-key block are keys
-//                 8j + 4(l/32) + i (j, i = 0..3).
-//   softmax       online, in base 2 (scale*log2(e) folded into one FMA); the
-//                 running row max is shared by the two lane halves through
-//                 one v_permlane32_swap per tile; row sums stay per half and
-//                 are added once at the end.
-//   O^T += V^T P^T  A = V^T (32 dims x 16 keys) read from LDS, B = P^T taken
-//                 straight from the S^T accumulators (8 consecutive
-//                 accumulator values = one 16-key k-step), so P never leaves
-//                 registers.
-// Workgroup: RW row-waves x KW key-waves.  All waves stage the same K/V
-// iteration tile (KW*KT keys) through LDS; key-wave kg processes keys
-// [kg*KT, (kg+1)*KT) of it.  K is stored row-major (padded pitch), V is
-// stored transposed [dim][key] with the key index's bits 2 and 3 swapped, so
-// that each lane's eight PV operands are 16 contiguous bytes.  The next
-// iteration tile is prefetched into registers while the current one is used.
-// With KW > 1 the key-waves' partial results are merged through LDS by the
-// same log-space rule.
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K (32 keys x 16 dims) from
+//                   LDS, B = Q^T held in registers.  Lane l owns query row
+//                   l%32; its 16 accumulators per 32-key block are keys
+//                   8j + 4(l/32) + i (j, i = 0..3).
+//   softmax         online, base 2 (scale*log2(e) folded into one FMA).  The
+//                   reference max is only moved when some row's max grew by
+//                   more than 2^8 (then all rows rescale), so most tiles skip
+//                   the rescale of the output accumulators.  The max is shared
+//                   by the two lane halves with one v_permlane32_swap per
+//                   tile; row sums stay per half until the end.
+//   O^T += V^T P^T  A = V^T (32 dims x 16 keys) gathered from row-major V in
+//                   LDS by two ds_read_b64_tr_b16 (each 16-lane group reads a
+//                   4-key x 16-dim block and receives it transposed), B = P^T
+//                   straight from the S^T accumulators (8 consecutive
+//                   accumulators = one 16-key step), so P never leaves
+//                   registers.
+// Staging: K and V tiles go from HBM to LDS with global_load_lds_dwordx4
+// (no register round trip) into an ST-deep ring of stages; a tile is waited
+// for with s_waitcnt vmcnt and one barrier per iteration, so ST-1 tiles are
+// in flight while one is consumed.  Rows of K and V are 2*d bytes; their
+// 16-byte chunks are XOR-swizzled by row so that both the 32-row K reads
+// (ds_read_b128) and the 4-row V transpose reads hit distinct banks.
+// Workgroup: RW row-waves x KW key-waves; key-wave kg takes keys
+// [kg*KT, (kg+1)*KT) of each KW*KT-key iteration tile, and the key-waves'
+// partial results are merged through LDS at the end.
+// Work mapping: work items are numbered so that the row tiles and key splits
+// sharing one (sequence, KV head) are consecutive, and consecutive items go
+// to the same XCD (workgroup i runs on XCD i % 8), so K/V re-reads hit that
+// XCD's L2.
 
 #include <math.h>
 
@@ -41,10 +50,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -61,48 +72,91 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+// 16 bytes from global memory straight into LDS: lane l's bytes land at
+// lds_base + 16*l (M0 holds the wave-uniform base).  Written as asm so the
+// compiler does not make every later LDS read wait for all DMA in flight;
+// completion is tracked explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
 }
 
-// Position of key `kk` (index within one key-wave's tile) in the transposed V
-// row: swap bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+// Wait until at most N vector-memory operations of this wave are in flight,
+// then barrier the workgroup.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int D, int RW, int KW, int KT>
-__global__ void __launch_bounds__(64 * RW * KW)
+// Cross-workgroup exchange of split partials: writers store with agent scope
+// (sc1: written through the XCD's L2) and wait for the acknowledgements
+// before taking their ticket, so no writer flushes its whole L2; only the one
+// workgroup that combines a tile invalidates its own L2 (which may hold stale
+// lines of the workspace) before reading the partials.
+__device__ __forceinline__ void st_agent1(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent4(float* p, f32x4 v) {
+  st_agent1(p, v[0]);
+  st_agent1(p + 1, v[1]);
+  st_agent1(p + 2, v[2]);
+  st_agent1(p + 3, v[3]);
+}
+__device__ __forceinline__ float ld_agent1(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void invalidate_l2() { asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1);
+}
+
+template <int D, int RW, int KW, int KT, int ST, bool GATED>
+__global__ void __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu(2)))
 attn_bf16_kernel(const AttnParams p) {
   constexpr int NW = RW * KW;
   constexpr int NT = 64 * NW;
-  constexpr int KTILE = KW * KT;                  // keys staged per iteration
-  constexpr int KP = D * 2 + 16;                  // K row pitch, bytes
-  constexpr int VP = KTILE * 2 + 16;              // V^T row pitch, bytes
-  constexpr int KS = D / 16;                      // MFMA k-steps over head dim
-  constexpr int DB = D / 32;                      // 32-dim output blocks
-  constexpr int MB = KT / 32;                     // 32-key blocks per key-wave
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int KTOT = KTILE * CPR;               // 16-byte K chunks per tile
-  constexpr int VTOT = (KTILE / 4) * CPR;         // 4-key x 8-dim V blocks per tile
-  constexpr int KCH = (KTOT + NT - 1) / NT;       // per thread
-  constexpr int VCH = (VTOT + NT - 1) / NT;
-  constexpr int SMEM_TILE = KTILE * KP + D * VP;
-  constexpr int XSLOT = (DB * 16 + 2) * 64;       // floats per exchange slot
+  constexpr int KTILE = KW * KT;                 // keys per iteration tile
+  constexpr int ROWB = D * 2;                    // bytes per K/V row
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  constexpr int RPB = 1024 / ROWB;               // rows per 1 KB DMA block
+  constexpr int TILE_B = KTILE * ROWB;           // bytes of one K (or V) tile
+  constexpr int NBLK = TILE_B / 1024;            // DMA blocks per K (or V) tile
+  constexpr int BPW = NBLK / NW;                 // DMA blocks per wave
+  constexpr int LPT = 2 * BPW;                   // DMA ops per thread per tile
+  constexpr int KS = D / 16;                     // MFMA k-steps over head dim
+  constexpr int DB = D / 32;                     // 32-dim output blocks
+  constexpr int MB = KT / 32;                    // 32-key blocks per key-wave
+  static_assert(NBLK % NW == 0 && BPW >= 1, "tile must split evenly into per-wave DMA blocks");
+  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int XSLOT = (DB * 16 + 2) * 64;      // floats per key-wave exchange slot
   constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
-  constexpr int SMEM = SMEM_TILE > SMEM_X ? SMEM_TILE : SMEM_X;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  unsigned char* const sK = smem;
-  unsigned char* const sV = smem + KTILE * KP;
+  constexpr int SMEM_R = ST * STAGE_B;
+  constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  __shared__ int s_last;
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rw = w % RW, kg = w / RW;
   const int lr = lane & 31, hf = lane >> 5;
 
-  const int split = blockIdx.x, rt = blockIdx.y;
-  const int b = blockIdx.z / p.hkv;
-  const int kvh = blockIdx.z - b * p.hkv;
+  // --- work item (XCD-aware numbering) ---
+  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= n_items) return;
+  const int split = item % p.n_splits;
+  const int rt = (item / p.n_splits) % p.row_tiles;
+  const int bz = item / (p.n_splits * p.row_tiles);
+  const int b = bz / p.hkv;
+  const int kvh = bz - b * p.hkv;
+
   const bool varlen = p.cu_q != nullptr;
   int qbase = 0, nq = p.max_q, kbase = 0, nk = p.max_k;
   if (varlen) {
@@ -116,30 +170,31 @@ attn_bf16_kernel(const AttnParams p) {
   const int row0 = rt * (RW * 32);
   if (row0 >= R) return;
   const int kb = split * p.chunk;
-  if (p.mode == kPrefixPartial && kb >= nk) return;
+  // A sequence with no keys at all is finished by split 0 alone (A = 0,
+  // L = -inf); otherwise splits past the end have nothing to do.
+  const int mode = (p.mode == kPrefixPartial && nk == 0) ? kPrefixFinal : p.mode;
+  if (p.mode == kPrefixPartial && kb >= nk && !(nk == 0 && split == 0)) return;
   const int ke = min(nk, kb + p.chunk);
-  const bool gated = p.decision != nullptr && p.mode != kBlock;
-  if (gated) {
+  if constexpr (GATED) {
     const int rlast = min(R, row0 + RW * 32) - 1;
     bool any = false;
     for (int g = row0 / nq; g <= rlast / nq; ++g) any |= p.decision[b * p.hq + kvh * G + g] == 0;
     if (!any) return;
   }
 
-  // This lane's query row.
+  // --- this lane's query row and its Q operand (B of S^T = K Q^T) ---
   const int r = row0 + rw * 32 + lr;
   const bool rvalid = r < R;
   const int g = rvalid ? r / nq : 0;
   const int i = rvalid ? r - g * nq : 0;
   const int h = kvh * G + g;
-
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
       (varlen ? (int64_t)(qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
       (int64_t)h * p.qs2;
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = rvalid ? ld16(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
+    u32x4 x = rvalid ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
     qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -148,51 +203,23 @@ attn_bf16_kernel(const AttnParams p) {
   const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
       (varlen ? (int64_t)kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VCH][4];
-  auto load_tile = [&](int t0) {
+  // DMA of one iteration tile (keys t0 .. t0+KTILE) into ring stage st.
+  // Lane l of a 1 KB block writes row blk*RPB + l/CPR, chunk slot l%CPR, which
+  // holds source chunk (l%CPR) ^ swz(row).  Keys past the range are clamped
+  // to the last valid key (finite data; their scores are masked).
+  const int l_row = lane / CPR;
+  const int l_slot = lane % CPR;
+  auto issue_tile = [&](int t0, int st) {
+    const unsigned kdst = smem_base + st * STAGE_B;
+    const unsigned vdst = kdst + TILE_B;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + NT * u;
-      const int key = c / CPR, col = c % CPR;
-      const int j = (KTOT % NT == 0 || c < KTOT) ? t0 + key : ke;
-      kreg[u] = (j < ke) ? ld16(kptr + (int64_t)j * p.ks1 + col * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int c = tid + NT * u;
-      const int kq = c / CPR, dg = c % CPR;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int j = (VTOT % NT == 0 || c < VTOT) ? t0 + 4 * kq + ii : ke;
-        vreg[u][ii] = (j < ke) ? ld16(vptr + (int64_t)j * p.vs1 + dg * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + NT * u;
-      if (KTOT % NT != 0 && c >= KTOT) break;
-      const int key = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(sK + key * KP + col * 16) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int c = tid + NT * u;
-      if (VTOT % NT != 0 && c >= VTOT) break;
-      const int kq = c / CPR, dg = c % CPR;
-      const int key0 = 4 * kq;
-      const int grp = key0 / KT;
-      const int pos = grp * KT + vt_pos(key0 - grp * KT);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const unsigned sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 pk;
-        pk[0] = __builtin_amdgcn_perm(vreg[u][1][dd >> 1], vreg[u][0][dd >> 1], sel);
-        pk[1] = __builtin_amdgcn_perm(vreg[u][3][dd >> 1], vreg[u][2][dd >> 1], sel);
-        *reinterpret_cast<u32x2*>(sV + (dg * 8 + dd) * VP + pos * 2) = pk;
-      }
+    for (int u = 0; u < BPW; ++u) {
+      const int blk = w * BPW + u;
+      const int row = blk * RPB + l_row;
+      const int c = l_slot ^ swz<D>(row);
+      const int j = min(t0 + row, ke - 1);
+      dma16(kptr + (int64_t)j * p.ks1 + c * 8, kdst + blk * 1024);
+      dma16(vptr + (int64_t)j * p.vs1 + c * 8, vdst + blk * 1024);
     }
   };
 
@@ -203,25 +230,45 @@ attn_bf16_kernel(const AttnParams p) {
   float l_run = 0.0f;
   const float c2 = p.scale_log2;
 
+  // V operand lanes: 16-lane group tq covers dims db*32 + (tq%2)*16 .. +15;
+  // source lane ts addresses key row k0 + ts/4, dims +4*(ts%4) .. +3, i.e.
+  // chunk 4db + 2(tq%2) + (ts%4)/2, half ts%2.
+  const int tq = lane >> 4, ts = lane & 15;
+
   const int n_iter = (ke > kb) ? (ke - kb + KTILE - 1) / KTILE : 0;
-  if (n_iter > 0) load_tile(kb);
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < n_iter) issue_tile(kb + s * KTILE, s);
+
   for (int it = 0; it < n_iter; ++it) {
+    const int ahead = min(ST - 2, n_iter - 1 - it);   // tiles issued after this one
+    if constexpr (ST == 2) {
+      wait_barrier<0>();
+    } else if constexpr (ST == 3) {
+      if (ahead >= 1) wait_barrier<LPT>(); else wait_barrier<0>();
+    } else {
+      if (ahead >= 2) wait_barrier<2 * LPT>();
+      else if (ahead == 1) wait_barrier<LPT>();
+      else wait_barrier<0>();
+    }
+    if (it + ST - 1 < n_iter) issue_tile(kb + (it + ST - 1) * KTILE, (it + ST - 1) % ST);
+
     const int t0 = kb + it * KTILE;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_iter) load_tile(t0 + KTILE);
     const int g0 = t0 + kg * KT;
     if (g0 >= ke) continue;
+    const unsigned char* sK = smem + (it % ST) * STAGE_B;
+    const unsigned char* sV = sK + TILE_B;
 
     f32x16 s[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       s[mb] = f32x16{};
-      const unsigned char* krow = sK + (kg * KT + mb * 32 + lr) * KP + hf * 16;
+      const int row = kg * KT + mb * 32 + lr;
+      const unsigned char* krow = sK + row * ROWB;
+      const int sw = swz<D>(row);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + hf) ^ sw) << 4));
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
       }
     }
@@ -239,22 +286,25 @@ attn_bf16_kernel(const AttnParams p) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = pair_max(mx) * c2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
     float ps = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[mb][e], c2, -m_new));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[mb][e], c2, -m_run));
         s[mb][e] = pv;
         ps += pv;
       }
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    l_run += ps;
 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -264,10 +314,22 @@ attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) pw[q] = pack_bf16(s[mb][8 * h2 + 2 * q], s[mb][8 * h2 + 2 * q + 1]);
         const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-        const unsigned char* vcol = sV + (kg * KT + mb * 32 + 16 * h2 + 8 * hf) * 2;
+        const int kbase16 = kg * KT + mb * 32 + 16 * h2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vcol + (db * 32 + lr) * VP);
+          const int c = 4 * db + 2 * (tq & 1) + ((ts & 3) >> 1);
+          i16x4 lo, hi;
+          {
+            const int row = kbase16 + 4 * hf + (ts >> 2);
+            const unsigned char* a = sV + row * ROWB + ((c ^ swz<D>(row)) << 4) + 8 * (ts & 1);
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+          }
+          {
+            const int row = kbase16 + 8 + 4 * hf + (ts >> 2);
+            const unsigned char* a = sV + row * ROWB + ((c ^ swz<D>(row)) << 4) + 8 * (ts & 1);
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+          }
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
         }
       }
@@ -277,7 +339,7 @@ attn_bf16_kernel(const AttnParams p) {
   float l_tot = pair_sum(l_run);
 
   if constexpr (KW > 1) {
-    __syncthreads();
+    wait_barrier<0>();
     float* xs = reinterpret_cast<float*>(smem);
     if (kg > 0) {
       float* slot = xs + ((kg - 1) * RW + rw) * XSLOT;
@@ -289,49 +351,124 @@ attn_bf16_kernel(const AttnParams p) {
       slot[(DB * 16 + 1) * 64 + lane] = l_tot;
     }
     __syncthreads();
-    if (kg > 0) return;
-    float mall = m_run;
+    if (kg == 0) {
+      float mall = m_run;
 #pragma unroll
-    for (int q = 1; q < KW; ++q) mall = fmaxf(mall, xs[((q - 1) * RW + rw) * XSLOT + (DB * 16) * 64 + lane]);
-    if (mall != -INFINITY) {
-      const float a0 = __builtin_amdgcn_exp2f(m_run - mall);
-      l_tot *= a0;
+      for (int q = 1; q < KW; ++q) mall = fmaxf(mall, xs[((q - 1) * RW + rw) * XSLOT + (DB * 16) * 64 + lane]);
+      if (mall != -INFINITY) {
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mall);
+        l_tot *= a0;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= a0;
+        for (int db = 0; db < DB; ++db) o[db] *= a0;
 #pragma unroll
-      for (int q = 1; q < KW; ++q) {
-        const float* slot = xs + ((q - 1) * RW + rw) * XSLOT;
-        const float aq = __builtin_amdgcn_exp2f(slot[(DB * 16) * 64 + lane] - mall);
-        l_tot += aq * slot[(DB * 16 + 1) * 64 + lane];
+        for (int q = 1; q < KW; ++q) {
+          const float* slot = xs + ((q - 1) * RW + rw) * XSLOT;
+          const float aq = __builtin_amdgcn_exp2f(slot[(DB * 16) * 64 + lane] - mall);
+          l_tot += aq * slot[(DB * 16 + 1) * 64 + lane];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] += aq * slot[(db * 16 + e) * 64 + lane];
+            for (int e = 0; e < 16; ++e) o[db][e] += aq * slot[(db * 16 + e) * 64 + lane];
+        }
       }
+      m_run = mall;
     }
-    m_run = mall;
   }
 
-  if (!rvalid) return;
-  if (gated && p.decision[b * p.hq + h] != 0) return;
-
+  bool writer = kg == 0 && rvalid;
+  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
   const bool has = l_tot > 0.0f;
   const float inv = has ? 1.0f / l_tot : 0.0f;
   const float L = has ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   const int64_t orow = varlen ? (int64_t)(qbase + i) : (int64_t)b * p.max_q + i;
   const int64_t oe = orow * p.hq + h;
 
-  if (p.mode != kBlock) {
-    float* a;
-    float* l;
-    if (p.mode == kPrefixFinal) {
-      a = p.a + oe * D;
-      l = p.l + oe;
-    } else {
-      const int64_t ve = ((int64_t)split * p.n_seq * p.max_q + (int64_t)b * p.max_q + i) * p.hq + h;
-      a = p.ws_a + ve * D;
-      l = p.ws_l + ve;
+  if (mode == kPrefixPartial) {
+    // Publish this split's partial result; the last split of the tile to
+    // finish (integer ticket) merges all of them in split order.
+    const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+    if (writer) {
+      const int64_t ve = (int64_t)split * n_entries + ((int64_t)b * p.max_q + i) * p.hq + h;
+      float* a = p.ws_a + ve * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 val = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
+                       o[db][4 * j + 3] * inv};
+          st_agent4(a + db * 32 + 8 * j + 4 * hf, val);
+        }
+      if (hf == 0) st_agent1(p.ws_l + ve, L);
     }
+    wait_stores();
+    __syncthreads();
+    const int64_t tile = (int64_t)bz * p.row_tiles + rt;
+    const int ns = (nk + p.chunk - 1) / p.chunk;
+    if (tid == 0) {
+      const int t = atomicAdd(p.tickets + tile, 1);
+      s_last = (t == ns - 1);
+      if (s_last) atomicExch(p.tickets + tile, 0);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    invalidate_l2();
+    // (1) per-row split weights into LDS, (2) weighted sum of the partials
+    // with the loads of a row issued together.
+    const int rend = min(R, row0 + RW * 32);
+    const int nr = rend - row0;
+    float* wsl = reinterpret_cast<float*>(smem);          // [RW*32][ns] weights
+    float* lfin = wsl + RW * 32 * ns;                      // [RW*32] final L
+    for (int idx = tid; idx < nr * ns; idx += NT) {
+      const int rr = idx / ns, c = idx - rr * ns;
+      const int gg = (row0 + rr) / nq, ii = (row0 + rr) - gg * nq;
+      const int64_t e = ((int64_t)b * p.max_q + ii) * p.hq + kvh * G + gg;
+      wsl[rr * ns + c] = ld_agent1(p.ws_l + c * n_entries + e);
+    }
+    __syncthreads();
+    for (int rr = tid; rr < nr; rr += NT) {
+      float mxr = -INFINITY;
+      for (int c = 0; c < ns; ++c) mxr = fmaxf(mxr, wsl[rr * ns + c]);
+      float den = 0.0f;
+      for (int c = 0; c < ns; ++c) {
+        const float wgt = __builtin_amdgcn_exp2f((wsl[rr * ns + c] - mxr) * kLog2e);
+        wsl[rr * ns + c] = wgt;
+        den += wgt;
+      }
+      const float rd = 1.0f / den;
+      for (int c = 0; c < ns; ++c) wsl[rr * ns + c] *= rd;
+      lfin[rr] = mxr + __logf(den);
+    }
+    __syncthreads();
+    constexpr int TPE = D / 4;                               // threads per row
+    const int t4 = tid % TPE;
+    for (int rr = tid / TPE; rr < nr; rr += NT / TPE) {
+      const int gg = (row0 + rr) / nq, ii = (row0 + rr) - gg * nq, hh = kvh * G + gg;
+      if constexpr (GATED) {
+        if (p.decision[b * p.hq + hh]) continue;
+      }
+      const int64_t e = ((int64_t)b * p.max_q + ii) * p.hq + hh;
+      const float* src = p.ws_a + e * D + 4 * t4;
+      const int64_t cs = n_entries * D;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int c = 0; c < ns; ++c) {
+        const float* x = src + c * cs;
+        const float wgt = wsl[rr * ns + c];
+        acc[0] += wgt * ld_agent1(x);
+        acc[1] += wgt * ld_agent1(x + 1);
+        acc[2] += wgt * ld_agent1(x + 2);
+        acc[3] += wgt * ld_agent1(x + 3);
+      }
+      const int64_t oo = (varlen ? (int64_t)(qbase + ii) : (int64_t)b * p.max_q + ii) * p.hq + hh;
+      *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t4) = acc;
+      if (t4 == 0) p.l[oo] = lfin[rr];
+    }
+    return;
+  }
+
+  if (!writer) return;
+
+  if (mode == kPrefixFinal) {
+    float* a = p.a + oe * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -340,7 +477,7 @@ attn_bf16_kernel(const AttnParams p) {
                      o[db][4 * j + 3] * inv};
         *reinterpret_cast<f32x4*>(a + db * 32 + 8 * j + 4 * hf) = val;
       }
-    if (hf == 0) *l = L;
+    if (hf == 0) p.l[oe] = L;
     return;
   }
 
@@ -388,96 +525,55 @@ attn_bf16_kernel(const AttnParams p) {
   }
 }
 
-// N-way log-space merge of the split-KV partials of one (row, head) entry.
-// D/4 threads per entry, 4 dims each.
-__global__ void __launch_bounds__(256) combine_kernel(const CombineParams p) {
-  const int tpe = p.d / 4;
-  const int epb = blockDim.x / tpe;
-  const int64_t e = (int64_t)blockIdx.x * epb + threadIdx.x / tpe;
-  const int t = threadIdx.x % tpe;
-  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
-  if (e >= n_entries) return;
-  const int h = (int)(e % p.hq);
-  const int64_t vrow = e / p.hq;
-  const int b = (int)(vrow / p.max_q);
-  const int i = (int)(vrow - (int64_t)b * p.max_q);
-  int nq = p.max_q, nk = p.max_k, qbase = 0;
-  if (p.cu_q) {
-    qbase = p.cu_q[b];
-    nq = p.cu_q[b + 1] - qbase;
-    nk = p.cu_k[b + 1] - p.cu_k[b];
-  }
-  if (i >= nq) return;
-  if (p.decision && p.decision[b * p.hq + h]) return;
-  const int64_t orow = p.cu_q ? (int64_t)(qbase + i) : vrow;
-  const int64_t oe = orow * p.hq + h;
-  float* a = p.a + oe * p.d + 4 * t;
-  const int ns = nk > 0 ? (nk + p.chunk - 1) / p.chunk : 0;
-  if (ns == 0) {
-    *reinterpret_cast<f32x4*>(a) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (t == 0) p.l[oe] = -INFINITY;
-    return;
-  }
-  const int64_t sl = n_entries;  // entries per split
-  float mx = -INFINITY;
-  for (int c = 0; c < ns; ++c) mx = fmaxf(mx, p.ws_l[c * sl + e]);
-  float den = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = 0; c < ns; ++c) {
-    const float wgt = __builtin_amdgcn_exp2f((p.ws_l[c * sl + e] - mx) * kLog2e);
-    den += wgt;
-    const f32x4 pa = *reinterpret_cast<const f32x4*>(p.ws_a + (c * sl + e) * p.d + 4 * t);
-    acc += wgt * pa;
-  }
-  const float rd = 1.0f / den;
-  *reinterpret_cast<f32x4*>(a) = acc * rd;
-  if (t == 0) p.l[oe] = mx + __logf(den);
-}
-
-template <int D, int RW, int KW, int KT>
+template <int D, int RW, int KW, int KT, int ST>
 hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
-  dim3 grid(p.n_splits, p.row_tiles, p.n_seq * p.hkv);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT>), grid, dim3(64 * RW * KW), 0, s, p);
+  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  dim3 grid(per_xcd * kXcds);
+  if (p.decision != nullptr && p.mode != kBlock)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), grid, dim3(64 * RW * KW), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), grid, dim3(64 * RW * KW), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Variants: 0 = 128 rows x 64 keys (4 row-waves), 1 = 64 rows x 2x32 keys,
-// 2 = 32 rows x 4x32 keys.  Fewer query rows per KV head -> more key-waves,
-// so a workgroup still keeps four waves busy.
+// Variants (rows per workgroup x keys per iteration tile, ring depth):
+//   0: 128 rows (4 row-waves) x 64 keys, 2 stages (64 KB LDS: 2 WG per CU)
+//   1:  64 rows (2 row-waves x 2 key-waves of 32) x 64 keys, 2 stages
+//   2:  32 rows (4 key-waves of 32) x 128 keys, 2 stages (128 KB LDS at d=128)
+// Fewer query rows per KV head -> more key-waves, so four waves stay busy.
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
-  (void)d;
   (void)max_k;
   (void)prefix;
-  if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64};
-  if (rows_per_kv_head > 32) return Bf16Plan{1, 64, 64};
-  return Bf16Plan{2, 32, 128};
+  if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64, 2};
+  if (rows_per_kv_head > 32) return Bf16Plan{1, 64, 64, 2};
+  return Bf16Plan{2, 32, 128, d == 128 ? 1 : 2};
+}
+
+// Largest split count whose combine weights ([rows][splits] floats plus one
+// final L per row) fit in the variant's LDS ring.
+int max_splits_bf16(int d, int variant) {
+  const int rows = variant == 0 ? 128 : (variant == 1 ? 64 : 32);
+  const int keys = variant == 2 ? 128 : 64;
+  const int ring_bytes = 2 * 2 * keys * d * 2;
+  return (ring_bytes / 4 - rows) / rows;
 }
 
 hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s) {
   if (d == 128) {
     switch (plan.variant) {
-      case 0: return launch_variant<128, 4, 1, 64>(p, s);
-      case 1: return launch_variant<128, 2, 2, 32>(p, s);
-      default: return launch_variant<128, 1, 4, 32>(p, s);
+      case 0: return launch_variant<128, 4, 1, 64, 2>(p, s);
+      case 1: return launch_variant<128, 2, 2, 32, 2>(p, s);
+      default: return launch_variant<128, 1, 4, 32, 2>(p, s);
     }
   }
   switch (plan.variant) {
-    case 0: return launch_variant<64, 4, 1, 64>(p, s);
-    case 1: return launch_variant<64, 2, 2, 32>(p, s);
-    default: return launch_variant<64, 1, 4, 32>(p, s);
+    case 0: return launch_variant<64, 4, 1, 64, 2>(p, s);
+    case 1: return launch_variant<64, 2, 2, 32, 2>(p, s);
+    default: return launch_variant<64, 1, 4, 32, 2>(p, s);
   }
-}
-
-hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  const int tpe = p.d / 4;
-  const int epb = 256 / tpe;
-  const int64_t n = (int64_t)p.n_seq * p.max_q * p.hq;
-  const int64_t blocks = (n + epb - 1) / epb;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
 }
 
 }  // namespace ba

@@ -100,14 +100,31 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   const int64_t items = (int64_t)d->n_seq * d->hkv * pp.row_tiles;
   const int kpi = pp.bf.keys_per_iter;
   const int64_t iters = (d->max_k + kpi - 1) / kpi;
-  // Aim for about two workgroups per compute unit (256 CUs), each streaming
-  // at least two iteration tiles.
-  const int64_t target = 512;
-  int64_t splits = items > 0 ? (target + items - 1) / items : 1;
-  const int64_t max_splits = iters / 2 > 1 ? iters / 2 : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int64_t chunk_iters = (iters + splits - 1) / splits;
+  // Pick the key-split count minimising a makespan estimate in units of one
+  // iteration tile: (rounds of workgroups over the 256 CUs) x (tiles per
+  // workgroup + 2 for pipeline fill and epilogue) + the combining
+  // workgroup's read of the partials (split count x rows per workgroup /
+  // keys per tile, since a tile of K+V and a partial row both carry 4*d
+  // bytes per row).
+  const int64_t slots = 256LL * pp.bf.wg_per_cu;
+  int64_t max_s = iters < 1 ? 1 : iters;
+  const int64_t lds_cap = ba::max_splits_bf16(d->d, pp.bf.variant);
+  if (max_s > lds_cap) max_s = lds_cap;
+  if (max_s > 64) max_s = 64;
+  int64_t best_s = 1;
+  double best_cost = 1e300;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t ci = (iters + s - 1) / s;
+    const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
+    const int64_t rounds = (items * se + slots - 1) / slots;
+    const double cost = (double)rounds * (double)(ci + 2) +
+                        (se > 1 ? (double)se * pp.bf.rows_per_wg / kpi : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best_s = se;
+    }
+  }
+  int64_t chunk_iters = (iters + best_s - 1) / best_s;
   if (chunk_iters < 1) chunk_iters = 1;
   pp.chunk = (int)(chunk_iters * kpi);
   pp.n_splits = d->max_k > 0 ? (int)((d->max_k + pp.chunk - 1) / pp.chunk) : 1;
@@ -115,10 +132,16 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   return pp;
 }
 
+// Workspace: [tickets int32, 256-byte aligned][partial A f32][partial L f32].
+size_t prefix_ticket_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
+  const size_t tiles = (size_t)d->n_seq * d->hkv * pp.row_tiles;
+  return (tiles * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
 size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
   if (pp.n_splits <= 1) return 0;
   const size_t entries = (size_t)d->n_seq * d->max_q * d->hq;
-  return (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float) + 256;
+  return prefix_ticket_bytes(d, pp) + (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float);
 }
 
 ba::AttnParams base_params(const ba_attn_desc* d, const AttnShape& sh) {
@@ -173,7 +196,8 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
-  if (pp.row_tiles > 65535) return fail(BA_ERR_UNSUPPORTED, "too many query rows per KV head");
+  if ((int64_t)pp.n_splits * pp.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
+    return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
   ba::AttnParams p = base_params(desc, sh);
   p.decision = desc->decision;
   p.chunk = pp.chunk;
@@ -193,26 +217,12 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
   }
   const size_t entries = (size_t)desc->n_seq * desc->max_q * desc->hq;
   p.mode = ba::kPrefixPartial;
-  p.ws_a = static_cast<float*>(workspace);
+  p.a = a_out;
+  p.l = l_out;
+  p.tickets = static_cast<int32_t*>(workspace);
+  p.ws_a = reinterpret_cast<float*>(static_cast<char*>(workspace) + prefix_ticket_bytes(desc, pp));
   p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
-  st = hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention (split)");
-  if (st != BA_OK) return st;
-  ba::CombineParams c{};
-  c.ws_a = p.ws_a;
-  c.ws_l = p.ws_l;
-  c.a = a_out;
-  c.l = l_out;
-  c.cu_q = desc->cu_q;
-  c.cu_k = desc->cu_k;
-  c.decision = desc->decision;
-  c.n_seq = desc->n_seq;
-  c.hq = desc->hq;
-  c.max_q = desc->max_q;
-  c.max_k = desc->max_k;
-  c.chunk = pp.chunk;
-  c.n_splits = pp.n_splits;
-  c.d = desc->d;
-  return hip_status(ba::launch_combine(c, stream), "split-KV combine");
+  return hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention (split)");
 }
 
 ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache, float* a_in,
@@ -241,7 +251,8 @@ ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const fl
   const int rows = sh.group * desc->max_q;
   const ba::Bf16Plan bf = ba::plan_bf16(desc->d, rows, desc->max_k, false);
   p.row_tiles = (rows + bf.rows_per_wg - 1) / bf.rows_per_wg;
-  if (p.row_tiles > 65535) return fail(BA_ERR_UNSUPPORTED, "too many query rows per KV head");
+  if ((int64_t)p.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
+    return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
   return hip_status(ba::launch_attn_bf16(bf, p, desc->d, stream), "block attention");
 }
 
@@ -276,6 +287,7 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, ui
   if (!decision) return fail(BA_ERR_NULL, "decision is required");
   const bool count = g->mode == BA_GATE_COUNT;
   if (count && !m_count) return fail(BA_ERR_NULL, "m_count is required in count mode");
+  if (count && g->n_blk > 65535) return fail(BA_ERR_UNSUPPORTED, "count gate supports n_blk <= 65535");
   if (count && !g->upd_mask) {
     if (!g->q_cur || !g->q_prev) return fail(BA_ERR_NULL, "q_cur and q_prev are required");
     if ((g->k_cur == nullptr) != (g->k_prev == nullptr) || (g->v_cur == nullptr) != (g->v_prev == nullptr))

@@ -37,34 +37,26 @@ struct AttnParams {
   float* l;
   float* ws_a;        // [n_splits][n_seq*max_q][hq][d]
   float* ws_l;        // [n_splits][n_seq*max_q][hq]
+  int32_t* tickets;   // [n_seq*hkv*row_tiles], zero between calls
   const float* a_cache;
   const float* l_cache;
   float* a_full;
   float* l_full;
 };
 
-struct CombineParams {
-  const float* ws_a;
-  const float* ws_l;
-  float* a;
-  float* l;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  const uint8_t* decision;
-  int n_seq, hq, max_q, max_k, chunk, n_splits, d;
-};
 
 // Launch-shape choice for the bf16 matrix-core kernel.
 struct Bf16Plan {
   int variant;        // index into the instantiated kernel table
   int rows_per_wg;    // query rows one workgroup covers
   int keys_per_iter;  // keys one workgroup stages per iteration
+  int wg_per_cu;      // workgroups that fit on one compute unit (LDS bound)
 };
 
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix);
+int max_splits_bf16(int d, int variant);
 hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
-hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
 struct MergeParams {
   int64_t rows;

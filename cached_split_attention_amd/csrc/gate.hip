@@ -9,7 +9,8 @@
 // (sequence, head) (cosine) finishes the reduction in a fixed order and
 // resets its ticket, so the workspace is zero again when the launch ends.
 // Only integer atomics are used; float64 partials are summed in chunk order,
-// so results are bitwise reproducible.
+// so results are bitwise reproducible.  Partials cross workgroups (and XCDs)
+// through agent-scope stores and loads, never through whole-cache flushes.
 
 #include <math.h>
 
@@ -63,19 +64,24 @@ __global__ void __launch_bounds__(256) gate_count_kernel(const GateParams p) {
     if (p.v_cur) diff |= rows_differ<W>(p.v_cur, p.v_prev, p.ks0, p.ks1, p.ks2, b, pos, p.hkv, rb, p.esize);
   }
   diff = __syncthreads_or(diff);
-  if (threadIdx.x != 0) return;
-  int32_t* acc = p.ws_int + 2 * b;
-  int32_t* ticket = acc + 1;
-  if (diff) atomicAdd(acc, 1);
-  __threadfence();
-  const int t = atomicAdd(ticket, 1);
-  if (t != p.n_blk - 1) return;
-  __threadfence();
-  const int m = atomicExch(acc, 0);
-  atomicExch(ticket, 0);
-  p.m_count[b] = m;
+  // One atomic per workgroup carries both the ticket (low 16 bits) and the
+  // count of changed positions (high 16 bits); the last workgroup of the
+  // sequence reads the total from its own return value and resets the word.
+  __shared__ int s_m;
+  if (threadIdx.x == 0) {
+    const unsigned old = atomicAdd(reinterpret_cast<unsigned*>(p.ws_int) + b, (diff ? 0x10000u : 0u) + 1u);
+    s_m = -1;
+    if ((int)(old & 0xffffu) == p.n_blk - 1) {
+      s_m = (int)(old >> 16) + (diff ? 1 : 0);
+      atomicExch(p.ws_int + b, 0);
+      p.m_count[b] = s_m;
+    }
+  }
+  __syncthreads();
+  const int m = s_m;
+  if (m < 0) return;
   const uint8_t dec = (p.cache_valid && m < p.tau) ? 1 : 0;
-  for (int h = 0; h < p.hq; ++h) p.decision[(int64_t)b * p.hq + h] = dec;
+  for (int h = threadIdx.x; h < p.hq; h += blockDim.x) p.decision[(int64_t)b * p.hq + h] = dec;
 }
 
 __device__ __forceinline__ float load_elem(const void* base, int64_t idx, int esize) {
@@ -120,11 +126,12 @@ __global__ void __launch_bounds__(256) gate_cos_kernel(const GateParams p) {
   st_agent(part + 0, red[0][0]);
   st_agent(part + 1, red[1][0]);
   st_agent(part + 2, red[2][0]);
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged before the ticket
   int32_t* ticket = p.ws_int + bh;
   const int t = atomicAdd(ticket, 1);
   if (t != p.chunks - 1) return;
-  __threadfence();
+  // The XCD's L2 may hold stale lines of the partials: drop them first.
+  asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
   double sd = 0.0, sc = 0.0, sp = 0.0;
   for (int k = 0; k < p.chunks; ++k) {
     double* q = p.ws_dbl + (bh * p.chunks + k) * 3;
@@ -158,7 +165,7 @@ int gate_cos_chunks(int n_blk, int d) {
 }
 
 size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d) {
-  if (mode == BA_GATE_COUNT) return (size_t)n_seq * 2 * sizeof(int32_t);
+  if (mode == BA_GATE_COUNT) return (size_t)n_seq * sizeof(int32_t);
   const size_t nbh = (size_t)n_seq * hq;
   const size_t ints = (nbh * sizeof(int32_t) + 15) & ~(size_t)15;
   return ints + nbh * gate_cos_chunks(n_blk, d) * 3 * sizeof(double);

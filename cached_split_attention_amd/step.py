@@ -49,23 +49,29 @@ class CachedBlockAttention:
         self._gws = None
 
     def start_block(self, kp=None, vp=None):
-        """Invalidate the cache (a new block begins; the prefix grew)."""
+        """Invalidate the cache (a new block begins; the prefix may have grown)."""
         if kp is not None:
+            if kp.shape != self.kp.shape:
+                self._ws = None
             self.kp, self.vp = kp, vp
-            self._ws = None
         self.cache_valid = False
 
     def _workspaces(self, q, k, v, q_prev, k_prev, v_prev):
         if self._ws is None:
             n = ba_prefix_attn_workspace(q, self.kp, self.vp, kv_layout=self.kv_layout, scale=self.scale)
-            self._ws = torch.empty(max(n, 1), device=q.device, dtype=torch.uint8)
+            self._ws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
         if self._gws is None:
             kw = {} if self.mode == BA_GATE_COSINE else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
             n = ba_reuse_gate_workspace(self.mode, q, q_prev, **kw)
             self._gws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
 
-    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None):
-        """Run one step; returns (a_full, l_full) views of the output buffers."""
+    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None, prefix_events=None):
+        """Run one step; returns (a_full, l_full) views of the output buffers.
+
+        With no valid cache the gate still runs (it reports M), but the prefix
+        pass is launched without the decision: everything recomputes.
+        prefix_events: optional (start, end) events recorded around the
+        prefix pass on the launch stream."""
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
         if self.mode == BA_GATE_COUNT:
             ba_reuse_gate(self.mode, q, q_prev, k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev,
@@ -74,8 +80,13 @@ class CachedBlockAttention:
         else:
             ba_reuse_gate(self.mode, q, q_prev, gamma=self.gamma, cache_valid=self.cache_valid,
                           cos=self.cos, decision=self.decision, workspace=self._gws, stream=stream)
+        if prefix_events is not None:
+            prefix_events[0].record(stream)
         ba_prefix_attn(q, self.kp, self.vp, self.a_out, self.l_out, self._ws, kv_layout=self.kv_layout,
-                       decision=self.decision, scale=self.scale, stream=stream)
+                       decision=self.decision if self.cache_valid else None, scale=self.scale,
+                       stream=stream)
+        if prefix_events is not None:
+            prefix_events[1].record(stream)
         ba_block_attn(q, k, v, a_cache=self.a_out, l_cache=self.l_out, a_full=self.a_full,
                       l_full=self.l_full, scale=self.scale, stream=stream)
         self.cache_valid = True

@@ -48,11 +48,11 @@ FAKE = 0x10000  # a non-NULL pointer value that is never dereferenced here
 
 def good_desc():
     d = lib_mod.AttnDesc()
-    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 1, 4, 2, 128, 32, 256
+    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 1, 4, 2, 128, 32, 8192
     d.q = d.k = d.v = FAKE
     for i, s in enumerate((32 * 4 * 128, 4 * 128, 128)):
         d.q_stride[i] = s
-    for i, s in enumerate((2 * 256 * 128, 128, 256 * 128)):
+    for i, s in enumerate((2 * 8192 * 128, 128, 8192 * 128)):
         d.k_stride[i] = s
         d.v_stride[i] = s
     return d
@@ -91,7 +91,7 @@ def test_prefix_null_desc_and_outputs(lib):
 def test_prefix_workspace_required(lib):
     d = good_desc()
     need = lib.ba_prefix_attn_workspace(ctypes.byref(d))
-    assert need > 0  # a 256-key prefix for 8 heads is split across workgroups
+    assert need > 0  # an 8192-key prefix for 2 KV heads is split across workgroups
     st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), FAKE, FAKE, FAKE, need - 1, None)
     assert st == 5 and "workspace" in msg
 
@@ -134,7 +134,7 @@ def good_gate():
 def test_gate_validation(lib):
     g = good_gate()
     need = lib.ba_reuse_gate_workspace(ctypes.byref(g))
-    assert need == 2 * 2 * 4
+    assert need == 2 * 4
     st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, None, FAKE, need, None)
     assert st == 1 and "decision" in msg
     st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, FAKE, FAKE, need - 1, None)

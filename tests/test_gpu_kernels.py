@@ -243,7 +243,7 @@ def test_prefix_attn(dtype, shape):
     s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=hash(shape) % 1000)
     want_a, want_l = _oracle_prefix(s)
     q, kp, vp = dev_in(s.q[0], dtype), dev_in(s.kp, dtype), dev_in(s.vp, dtype)
-    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
     a = torch.full((B * nb, hq, d), 777.0, device=DEV)
     l = torch.full((B * nb, hq), 777.0, device=DEV)
     ba.ba_prefix_attn(q, kp, vp, a, l, ws)
@@ -268,7 +268,7 @@ def test_prefix_attn_decision_leaves_cache_untouched(dtype):
     dec[0, :] = 1            # a whole sequence reused
     dec[1, :] = 0            # a whole sequence recomputed
     q, kp, vp = dev_in(s.q[0], dtype), dev_in(s.kp, dtype), dev_in(s.vp, dtype)
-    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
     a = torch.full((B * nb, hq, d), 123.0, device=DEV)
     l = torch.full((B * nb, hq), -55.0, device=DEV)
     ba.ba_prefix_attn(q, kp, vp, a, l, ws, decision=torch.from_numpy(dec).to(DEV))
@@ -304,7 +304,7 @@ def test_prefix_attn_bshd_layout(dtype):
     q = dev_in(s.q[0], dtype)
     kp = dev_in(s.kp, dtype).transpose(1, 2).contiguous()  # [B, Lp, Hkv, d]
     vp = dev_in(s.vp, dtype).transpose(1, 2).contiguous()
-    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(q, kp, vp, kv_layout="bshd")), device=DEV,
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp, kv_layout="bshd")), device=DEV,
                      dtype=torch.uint8)
     a = torch.empty(60, 4, 128, device=DEV)
     l = torch.empty(60, 4, device=DEV)
@@ -411,7 +411,7 @@ def test_varlen_attention(d):
     a_out = torch.full((n, vb.h, d), 3.0, device=DEV)
     l_out = torch.full((n, vb.h), 3.0, device=DEV)
     kw = dict(q_layout="thd", cu_q=cu_q, max_q=max_q)
-    ws = torch.empty(max(1, ba.ba_prefix_attn_workspace(qp, kp, vp, kv_layout="htd", cu_k=cu_kp,
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(qp, kp, vp, kv_layout="htd", cu_k=cu_kp,
                                                          max_k=int(vb.prefix_lens.max()), **kw)),
                      device=DEV, dtype=torch.uint8)
     ba.ba_prefix_attn(qp, kp, vp, a_out, l_out, ws, kv_layout="htd", cu_k=cu_kp,
