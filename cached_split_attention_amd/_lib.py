@@ -13,7 +13,8 @@ import os
 import torch  # noqa: F401  (must load the HIP runtime before libba.so)
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libba.so")
+# BA_LIB selects another build of the same C-ABI (e.g. a debug build).
+LIB_PATH = os.environ.get("BA_LIB") or os.path.join(PKG_DIR, "libba.so")
 
 BA_OK = 0
 STATUS_NAMES = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_DTYPE",

@@ -89,36 +89,16 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Cross-workgroup exchange of split partials: writers store with agent scope
-// (sc1: written through the XCD's L2) and wait for the acknowledgements
-// before taking their ticket, so no writer flushes its whole L2; only the one
-// workgroup that combines a tile invalidates its own L2 (which may hold stale
-// lines of the workspace) before reading the partials.
-__device__ __forceinline__ void st_agent1(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent4(float* p, f32x4 v) {
-  st_agent1(p, v[0]);
-  st_agent1(p + 1, v[1]);
-  st_agent1(p + 2, v[2]);
-  st_agent1(p + 3, v[3]);
-}
-__device__ __forceinline__ float ld_agent1(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void invalidate_l2() { asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int D>
 __device__ __forceinline__ int swz(int row) {
   return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1);
 }
 
 template <int D, int RW, int KW, int KT, int ST, bool GATED>
-__global__ void __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * RW * KW)
+    __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
 attn_bf16_kernel(const AttnParams p) {
   constexpr int NW = RW * KW;
-  constexpr int NT = 64 * NW;
   constexpr int KTILE = KW * KT;                 // keys per iteration tile
   constexpr int ROWB = D * 2;                    // bytes per K/V row
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -138,7 +118,6 @@ attn_bf16_kernel(const AttnParams p) {
   constexpr int SMEM_R = ST * STAGE_B;
   constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-  __shared__ int s_last;
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
@@ -384,10 +363,10 @@ attn_bf16_kernel(const AttnParams p) {
   const int64_t oe = orow * p.hq + h;
 
   if (mode == kPrefixPartial) {
-    // Publish this split's partial result; the last split of the tile to
-    // finish (integer ticket) merges all of them in split order.
-    const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+    // This split's partial result (normalised A and its L); the combine
+    // kernel merges the splits.
     if (writer) {
+      const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
       const int64_t ve = (int64_t)split * n_entries + ((int64_t)b * p.max_q + i) * p.hq + h;
       float* a = p.ws_a + ve * D;
 #pragma unroll
@@ -396,71 +375,9 @@ attn_bf16_kernel(const AttnParams p) {
         for (int j = 0; j < 4; ++j) {
           f32x4 val = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
                        o[db][4 * j + 3] * inv};
-          st_agent4(a + db * 32 + 8 * j + 4 * hf, val);
+          *reinterpret_cast<f32x4*>(a + db * 32 + 8 * j + 4 * hf) = val;
         }
-      if (hf == 0) st_agent1(p.ws_l + ve, L);
-    }
-    wait_stores();
-    __syncthreads();
-    const int64_t tile = (int64_t)bz * p.row_tiles + rt;
-    const int ns = (nk + p.chunk - 1) / p.chunk;
-    if (tid == 0) {
-      const int t = atomicAdd(p.tickets + tile, 1);
-      s_last = (t == ns - 1);
-      if (s_last) atomicExch(p.tickets + tile, 0);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    invalidate_l2();
-    // (1) per-row split weights into LDS, (2) weighted sum of the partials
-    // with the loads of a row issued together.
-    const int rend = min(R, row0 + RW * 32);
-    const int nr = rend - row0;
-    float* wsl = reinterpret_cast<float*>(smem);          // [RW*32][ns] weights
-    float* lfin = wsl + RW * 32 * ns;                      // [RW*32] final L
-    for (int idx = tid; idx < nr * ns; idx += NT) {
-      const int rr = idx / ns, c = idx - rr * ns;
-      const int gg = (row0 + rr) / nq, ii = (row0 + rr) - gg * nq;
-      const int64_t e = ((int64_t)b * p.max_q + ii) * p.hq + kvh * G + gg;
-      wsl[rr * ns + c] = ld_agent1(p.ws_l + c * n_entries + e);
-    }
-    __syncthreads();
-    for (int rr = tid; rr < nr; rr += NT) {
-      float mxr = -INFINITY;
-      for (int c = 0; c < ns; ++c) mxr = fmaxf(mxr, wsl[rr * ns + c]);
-      float den = 0.0f;
-      for (int c = 0; c < ns; ++c) {
-        const float wgt = __builtin_amdgcn_exp2f((wsl[rr * ns + c] - mxr) * kLog2e);
-        wsl[rr * ns + c] = wgt;
-        den += wgt;
-      }
-      const float rd = 1.0f / den;
-      for (int c = 0; c < ns; ++c) wsl[rr * ns + c] *= rd;
-      lfin[rr] = mxr + __logf(den);
-    }
-    __syncthreads();
-    constexpr int TPE = D / 4;                               // threads per row
-    const int t4 = tid % TPE;
-    for (int rr = tid / TPE; rr < nr; rr += NT / TPE) {
-      const int gg = (row0 + rr) / nq, ii = (row0 + rr) - gg * nq, hh = kvh * G + gg;
-      if constexpr (GATED) {
-        if (p.decision[b * p.hq + hh]) continue;
-      }
-      const int64_t e = ((int64_t)b * p.max_q + ii) * p.hq + hh;
-      const float* src = p.ws_a + e * D + 4 * t4;
-      const int64_t cs = n_entries * D;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int c = 0; c < ns; ++c) {
-        const float* x = src + c * cs;
-        const float wgt = wsl[rr * ns + c];
-        acc[0] += wgt * ld_agent1(x);
-        acc[1] += wgt * ld_agent1(x + 1);
-        acc[2] += wgt * ld_agent1(x + 2);
-        acc[3] += wgt * ld_agent1(x + 3);
-      }
-      const int64_t oo = (varlen ? (int64_t)(qbase + ii) : (int64_t)b * p.max_q + ii) * p.hq + hh;
-      *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t4) = acc;
-      if (t4 == 0) p.l[oo] = lfin[rr];
+      if (hf == 0) p.ws_l[ve] = L;
     }
     return;
   }
@@ -525,6 +442,65 @@ attn_bf16_kernel(const AttnParams p) {
   }
 }
 
+
+// N-way log-space merge of the split-KV partials (the merge equation applied
+// across key splits).  D/4 threads per (row, head) entry, four dims each; the
+// L and A partials of up to 8 splits are loaded together, so one memory
+// round trip serves a batch.
+template <int D>
+__global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
+  constexpr int TPE = D / 4;
+  constexpr int EPB = 256 / TPE;
+  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  const int64_t e = (int64_t)blockIdx.x * EPB + threadIdx.x / TPE;
+  const int t = threadIdx.x % TPE;
+  if (e >= n_entries) return;
+  const int h = (int)(e % p.hq);
+  const int64_t vrow = e / p.hq;
+  const int b = (int)(vrow / p.max_q);
+  const int i = (int)(vrow - (int64_t)b * p.max_q);
+  int nq = p.max_q, nk = p.max_k, qbase = 0;
+  if (p.cu_q) {
+    qbase = p.cu_q[b];
+    nq = p.cu_q[b + 1] - qbase;
+    nk = p.cu_k[b + 1] - p.cu_k[b];
+  }
+  if (i >= nq || nk == 0) return;  // empty prefix: written by the attention kernel
+  if (p.decision && p.decision[b * p.hq + h]) return;
+  const int ns = (nk + p.chunk - 1) / p.chunk;
+  const float* la = p.ws_l + e;
+  const float* aa = p.ws_a + e * D + 4 * t;
+  const int64_t cs = n_entries;
+  float mx = -INFINITY, den = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < ns; c0 += 8) {
+    float lv[8];
+    f32x4 av[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = c0 + u < ns;
+      lv[u] = ok ? la[(c0 + u) * cs] : -INFINITY;
+      av[u] = ok ? *reinterpret_cast<const f32x4*>(aa + (c0 + u) * cs * D) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float bm = mx;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bm = fmaxf(bm, lv[u]);
+    const float r = __builtin_amdgcn_exp2f((mx - bm) * kLog2e);  // rescale earlier batches
+    den *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wgt = __builtin_amdgcn_exp2f((lv[u] - bm) * kLog2e);
+      den += wgt;
+      acc += wgt * av[u];
+    }
+    mx = bm;
+  }
+  const int64_t oo = (p.cu_q ? (int64_t)(qbase + i) : vrow) * p.hq + h;
+  *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t) = acc * (1.0f / den);
+  if (t == 0) p.l[oo] = mx + __logf(den);
+}
+
 template <int D, int RW, int KW, int KT, int ST>
 hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
   const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
@@ -534,6 +510,11 @@ hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), grid, dim3(64 * RW * KW), 0, s, p);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), grid, dim3(64 * RW * KW), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.mode != kPrefixPartial) return err;
+  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  const int64_t epb = 256 / (D / 4);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((n_entries + epb - 1) / epb)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -552,13 +533,10 @@ Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
   return Bf16Plan{2, 32, 128, d == 128 ? 1 : 2};
 }
 
-// Largest split count whose combine weights ([rows][splits] floats plus one
-// final L per row) fit in the variant's LDS ring.
 int max_splits_bf16(int d, int variant) {
-  const int rows = variant == 0 ? 128 : (variant == 1 ? 64 : 32);
-  const int keys = variant == 2 ? 128 : 64;
-  const int ring_bytes = 2 * 2 * keys * d * 2;
-  return (ring_bytes / 4 - rows) / rows;
+  (void)d;
+  (void)variant;
+  return 256;
 }
 
 hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s) {

@@ -132,16 +132,11 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   return pp;
 }
 
-// Workspace: [tickets int32, 256-byte aligned][partial A f32][partial L f32].
-size_t prefix_ticket_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
-  const size_t tiles = (size_t)d->n_seq * d->hkv * pp.row_tiles;
-  return (tiles * sizeof(int32_t) + 255) & ~(size_t)255;
-}
-
+// Workspace: [partial A f32 [splits][entries][d]][partial L f32 [splits][entries]].
 size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
   if (pp.n_splits <= 1) return 0;
   const size_t entries = (size_t)d->n_seq * d->max_q * d->hq;
-  return prefix_ticket_bytes(d, pp) + (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float);
+  return (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float);
 }
 
 ba::AttnParams base_params(const ba_attn_desc* d, const AttnShape& sh) {
@@ -219,8 +214,7 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
   p.mode = ba::kPrefixPartial;
   p.a = a_out;
   p.l = l_out;
-  p.tickets = static_cast<int32_t*>(workspace);
-  p.ws_a = reinterpret_cast<float*>(static_cast<char*>(workspace) + prefix_ticket_bytes(desc, pp));
+  p.ws_a = static_cast<float*>(workspace);
   p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
   return hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention (split)");
 }

@@ -37,7 +37,6 @@ struct AttnParams {
   float* l;
   float* ws_a;        // [n_splits][n_seq*max_q][hq][d]
   float* ws_l;        // [n_splits][n_seq*max_q][hq]
-  int32_t* tickets;   // [n_seq*hkv*row_tiles], zero between calls
   const float* a_cache;
   const float* l_cache;
   float* a_full;

@@ -104,9 +104,8 @@ typedef struct ba_attn_desc {
  * prefix gives A_out = 0, L_out = -inf.
  * The key range is split across workgroups; partial results go to
  * `workspace`, whose size ba_prefix_attn_workspace() returns (0 means none is
- * needed and workspace may be NULL).  The workspace must be zero-filled
- * before its first use; every call leaves the words it relies on at zero, so
- * later calls need no re-initialisation.  One workspace per stream.
+ * needed and workspace may be NULL).  The workspace needs no
+ * initialisation; calls that overlap in time must not share one.
  */
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc);
 ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
