@@ -202,6 +202,24 @@ attn_bf16_kernel(const AttnParams p) {
     }
   };
 
+  // Single-wave workgroups serve small in-block problems, where the cache read
+  // of the merge would otherwise be one more memory round trip after the
+  // compute: fetch this lane's cached A_out/L_out now.
+  constexpr bool kPrefetchCache = (NW == 1);
+  f32x4 cache_a[kPrefetchCache ? 4 * DB : 1];
+  float cache_l = 0.0f;
+  if constexpr (kPrefetchCache) {
+    if (p.mode == kBlock && p.a_cache && rvalid) {
+      const int64_t ce = (varlen ? (int64_t)(qbase + i) : (int64_t)b * p.max_q + i) * p.hq + h;
+      cache_l = p.l_cache[ce];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          cache_a[db * 4 + j] = *reinterpret_cast<const f32x4*>(p.a_cache + ce * D + db * 32 + 8 * j + 4 * hf);
+    }
+  }
+
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
@@ -412,7 +430,8 @@ attn_bf16_kernel(const AttnParams p) {
   }
   if (p.l && hf == 0) p.l[oe] = L;
   if (p.a_cache) {
-    const float lc = p.l_cache[oe];
+    float lc;
+    if constexpr (kPrefetchCache) lc = cache_l; else lc = p.l_cache[oe];
     const float mm = fmaxf(lc, L);
     float wc = 0.0f, wi = 0.0f, lf = -INFINITY, rden = 0.0f;
     if (mm != -INFINITY) {
@@ -431,7 +450,8 @@ attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int c0 = db * 32 + 8 * j + 4 * hf;
-          const f32x4 cv = *reinterpret_cast<const f32x4*>(ac + c0);
+          f32x4 cv;
+          if constexpr (kPrefetchCache) cv = cache_a[db * 4 + j]; else cv = *reinterpret_cast<const f32x4*>(ac + c0);
           f32x4 val;
 #pragma unroll
           for (int e = 0; e < 4; ++e) val[e] = fc * cv[e] + fi * o[db][4 * j + e];
@@ -520,17 +540,17 @@ hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Variants (rows per workgroup x keys per iteration tile, ring depth):
-//   0: 128 rows (4 row-waves) x 64 keys, 2 stages (64 KB LDS: 2 WG per CU)
-//   1:  64 rows (2 row-waves x 2 key-waves of 32) x 64 keys, 2 stages
-//   2:  32 rows (4 key-waves of 32) x 128 keys, 2 stages (128 KB LDS at d=128)
-// Fewer query rows per KV head -> more key-waves, so four waves stay busy.
+// Variants (rows per workgroup x keys per iteration tile, 2-stage ring):
+//   0: 128 rows (4 row-waves) x 64 keys (64 KB LDS at d=128: 2 WG per CU)
+//   1:  64 rows (2 row-waves x 2 key-waves of 32) x 64 keys (2 WG per CU);
+//       also used for fewer rows: the streaming, not the MFMA, sets the pace
+//   2:  32 rows x 32 keys, one wave (8 KB LDS at d=128): small in-block
+//       problems, where latency dominates
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
-  (void)max_k;
-  (void)prefix;
+  (void)d;
   if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64, 2};
-  if (rows_per_kv_head > 32) return Bf16Plan{1, 64, 64, 2};
-  return Bf16Plan{2, 32, 128, d == 128 ? 1 : 2};
+  if (rows_per_kv_head <= 32 && max_k <= 64 && !prefix) return Bf16Plan{2, 32, 32, 8};
+  return Bf16Plan{1, 64, 64, 2};
 }
 
 int max_splits_bf16(int d, int variant) {
@@ -544,13 +564,13 @@ hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hi
     switch (plan.variant) {
       case 0: return launch_variant<128, 4, 1, 64, 2>(p, s);
       case 1: return launch_variant<128, 2, 2, 32, 2>(p, s);
-      default: return launch_variant<128, 1, 4, 32, 2>(p, s);
+      default: return launch_variant<128, 1, 1, 32, 2>(p, s);
     }
   }
   switch (plan.variant) {
     case 0: return launch_variant<64, 4, 1, 64, 2>(p, s);
     case 1: return launch_variant<64, 2, 2, 32, 2>(p, s);
-    default: return launch_variant<64, 1, 4, 32, 2>(p, s);
+    default: return launch_variant<64, 1, 1, 32, 2>(p, s);
   }
 }
 

@@ -101,24 +101,22 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   const int kpi = pp.bf.keys_per_iter;
   const int64_t iters = (d->max_k + kpi - 1) / kpi;
   // Pick the key-split count minimising a makespan estimate in units of one
-  // iteration tile: (rounds of workgroups over the 256 CUs) x (tiles per
-  // workgroup + 2 for pipeline fill and epilogue) + the combining
-  // workgroup's read of the partials (split count x rows per workgroup /
-  // keys per tile, since a tile of K+V and a partial row both carry 4*d
-  // bytes per row).
+  // iteration tile of one workgroup: (rounds of workgroups over all slots) x
+  // (tiles per workgroup + 2 for pipeline fill and epilogue), plus, with
+  // more than one split, the combine launch (~2) and its traffic (partials
+  // written and read, relative to the K/V bytes all slots stream per tile).
   const int64_t slots = 256LL * pp.bf.wg_per_cu;
   int64_t max_s = iters < 1 ? 1 : iters;
   const int64_t lds_cap = ba::max_splits_bf16(d->d, pp.bf.variant);
   if (max_s > lds_cap) max_s = lds_cap;
-  if (max_s > 64) max_s = 64;
   int64_t best_s = 1;
   double best_cost = 1e300;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
     const int64_t rounds = (items * se + slots - 1) / slots;
-    const double cost = (double)rounds * (double)(ci + 2) +
-                        (se > 1 ? (double)se * pp.bf.rows_per_wg / kpi : 0.0);
+    const double comb = se > 1 ? 2.0 + 2.0 * (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
+    const double cost = (double)rounds * (double)(ci + 2) + comb;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_s = se;

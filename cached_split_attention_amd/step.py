@@ -91,3 +91,35 @@ class CachedBlockAttention:
                       l_full=self.l_full, scale=self.scale, stream=stream)
         self.cache_valid = True
         return self.a_full, self.l_full
+
+    def capture(self, q, k, v, steps, new_block=True, kp=None, vp=None):
+        """Capture the given steps of a block's schedule as one HIP graph.
+
+        q, k, v: sequences of block tensors, index 0 = the block before step 1,
+        index t = the block at step t.  With new_block the graph starts a new
+        block (no valid cache); otherwise the cache is taken as valid.
+        Replaying the graph re-runs those steps on the same buffers.
+        Workspaces are allocated before capture and no memset is recorded
+        (the gate's workspace is cleared by its own kernels), so replays need
+        no re-initialisation.
+        """
+        steps = list(steps)
+        self.start_block(kp, vp)
+        t0 = steps[0]
+        self._workspaces(q[t0], k[t0], v[t0], q[t0 - 1], k[t0 - 1], v[t0 - 1])
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.cache_valid = not new_block
+                for t in steps:
+                    self.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1],
+                              stream=torch.cuda.current_stream())
+        torch.cuda.current_stream().wait_stream(side)
+        self.cache_valid = True
+        return graph
+
+    def capture_block(self, q, k, v, kp=None, vp=None):
+        """One block's whole schedule (steps 1 .. len(q)-1) as one graph."""
+        return self.capture(q, k, v, range(1, len(q)), new_block=True, kp=kp, vp=vp)

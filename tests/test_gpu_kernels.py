@@ -473,3 +473,35 @@ def test_schedule_bf16(schedule, gate):
                             schedule=schedule, redraw_range=(0, 3), poisson_lam=1.5,
                             sigma_range=(0.01, 0.5), gate=gate, tau=3, gamma=0.95, seed=67)
     assert _run_schedule(s) > 0
+
+
+def test_graph_replay_matches_eager():
+    """A captured block schedule replays to the eager result, every time,
+    with eager work and synchronisations between the replays."""
+    s = make_block_schedule(dtype="bf16", B=2, hq=4, hkv=2, d=128, lp=900, nb=33, steps=4, std=1.0,
+                            schedule="redraw", redraw_range=(0, 3), gate="count", tau=2, seed=68)
+    kp, vp = dev_bits(s.kp), dev_bits(s.vp)
+    q = [dev_bits(x) for x in s.q]
+    k = [dev_bits(x) for x in s.k]
+    v = [dev_bits(x) for x in s.v]
+    eager = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate="count", tau=s.tau)
+    outs = []
+    for t in range(1, s.steps + 1):
+        af, lf = eager.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+        outs.append((af.clone(), lf.clone(), eager.a_out.clone(), eager.decision.clone()))
+    torch.cuda.synchronize()
+    attn = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate="count", tau=s.tau)
+    g = attn.capture_block(q, k, v)
+    g1 = attn.capture(q, k, v, [s.steps], new_block=False)
+    for rep in range(3):
+        attn.a_full.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(attn.a_full, outs[-1][0]) and torch.equal(attn.l_full, outs[-1][1]), rep
+        assert torch.equal(attn.a_out, outs[-1][2]) and torch.equal(attn.decision, outs[-1][3]), rep
+        junk = torch.randn(1000, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+        g1.replay()   # the last step alone, cache valid
+        torch.cuda.synchronize()
+        assert torch.equal(attn.a_full, outs[-1][0]), rep
