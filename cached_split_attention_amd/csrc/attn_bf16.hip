@@ -24,14 +24,24 @@
 //                   accumulators = one 16-key step), so P never leaves
 //                   registers.
 // Staging: K and V tiles go from HBM to LDS with global_load_lds_dwordx4
-// (no register round trip) into an ST-deep ring of stages; a tile is waited
-// for with s_waitcnt vmcnt and one barrier per iteration, so ST-1 tiles are
-// in flight while one is consumed.  Rows of K and V are 2*d bytes; their
-// 16-byte chunks are XOR-swizzled by row so that both the 32-row K reads
-// (ds_read_b128) and the 4-row V transpose reads hit distinct banks.
-// Workgroup: RW row-waves x KW key-waves; key-wave kg takes keys
-// [kg*KT, (kg+1)*KT) of each KW*KT-key iteration tile, and the key-waves'
-// partial results are merged through LDS at the end.
+// (no register round trip) into a ring of stages; a tile is waited for with
+// s_waitcnt vmcnt and a workgroup barrier, so later tiles stay in flight
+// while one is consumed.  Rows of K and V are 2*d bytes; their 16-byte chunks
+// are XOR-swizzled by row so that both the 32-row K reads (ds_read_b128) and
+// the 4-row V transpose reads hit distinct banks.
+//
+// Two workgroup shapes:
+//   attn_bf16_kernel  RW row-waves x KW key-waves, one barrier per tile; key
+//                     wave kg takes keys [kg*KT, (kg+1)*KT) of each tile and
+//                     the key-waves' partial results are merged through LDS
+//                     at the end.  Serves short and medium row counts.
+//   attn_pp_kernel    eight waves over 256 rows in two groups of four that
+//                     alternate between a matrix phase (P.V of the previous
+//                     tile, then the scores of the next) and a vector phase
+//                     (softmax of those scores), half a tile apart: while one
+//                     group's wave on a SIMD issues MFMAs the other's issues
+//                     the exponentials, so the matrix cores are not left idle
+//                     during the softmax.  Serves long row counts.
 // Work mapping: work items are numbered so that the row tiles and key splits
 // sharing one (sequence, KV head) are consecutive, and consecutive items go
 // to the same XCD (workgroup i runs on XCD i % 8), so K/V re-reads hit that
@@ -57,14 +67,33 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag
 constexpr int kXcds = 8;
 
+// IEEE maximum (NaN-propagating): maps to v_maximum3_f32 without the operand
+// canonicalisation the C fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max over the score accumulators of MB 32-key blocks, as four independent
+// chains of 3-input maxima.
+template <int MB>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[MB]) {
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const int c = (e >> 1) & 3;
+      m[c] = vmax(vmax(m[c], s[mb][e]), s[mb][e + 1]);
+    }
+  return vmax(vmax(m[0], m[1]), vmax(m[2], m[3]));
 }
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
@@ -81,6 +110,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
 }
 
+// As dma16, from a wave-uniform base plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(base) : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight,
 // then barrier the workgroup.  The memory clobber keeps the compiler from
 // moving LDS accesses across it.
@@ -89,303 +124,230 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1);
+// As wait_barrier, also draining this wave's LDS reads first, with nothing
+// scheduled across it: a phase boundary of the alternating kernel.
+template <int N>
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int RW, int KW, int KT, int ST, bool GATED>
-__global__ void __launch_bounds__(64 * RW * KW)
-    __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
-attn_bf16_kernel(const AttnParams p) {
-  constexpr int NW = RW * KW;
-  constexpr int KTILE = KW * KT;                 // keys per iteration tile
-  constexpr int ROWB = D * 2;                    // bytes per K/V row
-  constexpr int CPR = D / 8;                     // 16-byte chunks per row
-  constexpr int RPB = 1024 / ROWB;               // rows per 1 KB DMA block
-  constexpr int TILE_B = KTILE * ROWB;           // bytes of one K (or V) tile
-  constexpr int NBLK = TILE_B / 1024;            // DMA blocks per K (or V) tile
-  constexpr int BPW = NBLK / NW;                 // DMA blocks per wave
-  constexpr int LPT = 2 * BPW;                   // DMA ops per thread per tile
-  constexpr int KS = D / 16;                     // MFMA k-steps over head dim
-  constexpr int DB = D / 32;                     // 32-dim output blocks
-  constexpr int MB = KT / 32;                    // 32-key blocks per key-wave
+// 16-byte chunk swizzle of a K/V row in LDS (d = 128: 16 chunks, 256 bytes =
+// one sweep of the 64 banks).  Swapping the two 2-bit halves of the row's low
+// nibble makes (a) the 16 rows one ds_read_b128 phase reads at the same chunk
+// land on 16 distinct chunks and (b) the 4 rows of a transposed V read land
+// in 4 distinct 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row & 3) << 1);
+}
+
+// DMA of K/V iteration tiles (KTILE keys) into LDS, shared by the NW waves of
+// a workgroup: wave w fetches 1 KB blocks w*BPW .. w*BPW+BPW-1 of the K tile
+// and of the V tile.  Lane l of a block writes row blk*RPB + l/CPR, chunk slot
+// l%CPR, which holds source chunk (l%CPR) ^ swz(row).  A full tile is fetched
+// from the tile's scalar base plus fixed per-lane byte offsets; the tail tile
+// clamps keys past the range to the last valid key (finite data; their scores
+// are masked).
+template <int D, int NW, int KTILE>
+struct TileDma {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int RPB = 1024 / ROWB;
+  static constexpr int TILE_B = KTILE * ROWB;
+  static constexpr int NBLK = TILE_B / 1024;
+  static constexpr int BPW = NBLK / NW;
+  static constexpr int OPS = 2 * BPW;  // vector-memory operations per wave per tile
   static_assert(NBLK % NW == 0 && BPW >= 1, "tile must split evenly into per-wave DMA blocks");
-  static_assert(ST >= 2 && ST <= 4, "ring depth");
-  constexpr int STAGE_B = 2 * TILE_B;
-  constexpr int XSLOT = (DB * 16 + 2) * 64;      // floats per key-wave exchange slot
-  constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
-  constexpr int SMEM_R = ST * STAGE_B;
-  constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-  const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int rw = w % RW, kg = w / RW;
-  const int lr = lane & 31, hf = lane >> 5;
+  const uint16_t* kptr;
+  const uint16_t* vptr;
+  int64_t ks1, vs1;
+  int ke, w, l_row, l_slot;
+  bool fast;
+  unsigned koffs[BPW], voffs[BPW];
 
-  // --- work item (XCD-aware numbering) ---
-  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= n_items) return;
-  const int split = item % p.n_splits;
-  const int rt = (item / p.n_splits) % p.row_tiles;
-  const int bz = item / (p.n_splits * p.row_tiles);
-  const int b = bz / p.hkv;
-  const int kvh = bz - b * p.hkv;
-
-  const bool varlen = p.cu_q != nullptr;
-  int qbase = 0, nq = p.max_q, kbase = 0, nk = p.max_k;
-  if (varlen) {
-    qbase = p.cu_q[b];
-    nq = p.cu_q[b + 1] - qbase;
-    kbase = p.cu_k[b];
-    nk = p.cu_k[b + 1] - kbase;
-  }
-  const int G = p.group;
-  const int R = G * nq;
-  const int row0 = rt * (RW * 32);
-  if (row0 >= R) return;
-  const int kb = split * p.chunk;
-  // A sequence with no keys at all is finished by split 0 alone (A = 0,
-  // L = -inf); otherwise splits past the end have nothing to do.
-  const int mode = (p.mode == kPrefixPartial && nk == 0) ? kPrefixFinal : p.mode;
-  if (p.mode == kPrefixPartial && kb >= nk && !(nk == 0 && split == 0)) return;
-  const int ke = min(nk, kb + p.chunk);
-  if constexpr (GATED) {
-    const int rlast = min(R, row0 + RW * 32) - 1;
-    bool any = false;
-    for (int g = row0 / nq; g <= rlast / nq; ++g) any |= p.decision[b * p.hq + kvh * G + g] == 0;
-    if (!any) return;
-  }
-
-  // --- this lane's query row and its Q operand (B of S^T = K Q^T) ---
-  const int r = row0 + rw * 32 + lr;
-  const bool rvalid = r < R;
-  const int g = rvalid ? r / nq : 0;
-  const int i = rvalid ? r - g * nq : 0;
-  const int h = kvh * G + g;
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-      (varlen ? (int64_t)(qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
-      (int64_t)h * p.qs2;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = rvalid ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
-  }
-
-  const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
-      (varlen ? (int64_t)kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
-  const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
-      (varlen ? (int64_t)kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
-
-  // DMA of one iteration tile (keys t0 .. t0+KTILE) into ring stage st.
-  // Lane l of a 1 KB block writes row blk*RPB + l/CPR, chunk slot l%CPR, which
-  // holds source chunk (l%CPR) ^ swz(row).  Keys past the range are clamped
-  // to the last valid key (finite data; their scores are masked).
-  const int l_row = lane / CPR;
-  const int l_slot = lane % CPR;
-  auto issue_tile = [&](int t0, int st) {
-    const unsigned kdst = smem_base + st * STAGE_B;
-    const unsigned vdst = kdst + TILE_B;
+  __device__ __forceinline__ TileDma(const uint16_t* kp, const uint16_t* vp, int64_t ks, int64_t vs, int kend,
+                                     int wave, int lane)
+      : kptr(kp), vptr(vp), ks1(ks), vs1(vs), ke(kend), w(wave), l_row(lane / CPR), l_slot(lane % CPR) {
+    fast = (int64_t)KTILE * (ks1 > vs1 ? ks1 : vs1) * 2 < (1LL << 31);
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
-      const int blk = w * BPW + u;
-      const int row = blk * RPB + l_row;
+      const int row = (w * BPW + u) * RPB + l_row;
       const int c = l_slot ^ swz<D>(row);
-      const int j = min(t0 + row, ke - 1);
-      dma16(kptr + (int64_t)j * p.ks1 + c * 8, kdst + blk * 1024);
-      dma16(vptr + (int64_t)j * p.vs1 + c * 8, vdst + blk * 1024);
-    }
-  };
-
-  // Single-wave workgroups serve small in-block problems, where the cache read
-  // of the merge would otherwise be one more memory round trip after the
-  // compute: fetch this lane's cached A_out/L_out now.
-  constexpr bool kPrefetchCache = (NW == 1);
-  f32x4 cache_a[kPrefetchCache ? 4 * DB : 1];
-  float cache_l = 0.0f;
-  if constexpr (kPrefetchCache) {
-    if (p.mode == kBlock && p.a_cache && rvalid) {
-      const int64_t ce = (varlen ? (int64_t)(qbase + i) : (int64_t)b * p.max_q + i) * p.hq + h;
-      cache_l = p.l_cache[ce];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          cache_a[db * 4 + j] = *reinterpret_cast<const f32x4*>(p.a_cache + ce * D + db * 32 + 8 * j + 4 * hf);
+      koffs[u] = fast ? (unsigned)((row * ks1 + c * 8) * 2) : 0u;
+      voffs[u] = fast ? (unsigned)((row * vs1 + c * 8) * 2) : 0u;
     }
   }
 
-  f32x16 o[DB];
+  __device__ __forceinline__ void issue(int t0, unsigned kdst, unsigned vdst) const {
+    if (fast && t0 + KTILE <= ke) {
+      const uint16_t* kt = kptr + (int64_t)t0 * ks1;
+      const uint16_t* vt = vptr + (int64_t)t0 * vs1;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-  const float c2 = p.scale_log2;
-
-  // V operand lanes: 16-lane group tq covers dims db*32 + (tq%2)*16 .. +15;
-  // source lane ts addresses key row k0 + ts/4, dims +4*(ts%4) .. +3, i.e.
-  // chunk 4db + 2(tq%2) + (ts%4)/2, half ts%2.
-  const int tq = lane >> 4, ts = lane & 15;
-
-  const int n_iter = (ke > kb) ? (ke - kb + KTILE - 1) / KTILE : 0;
-#pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < n_iter) issue_tile(kb + s * KTILE, s);
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int ahead = min(ST - 2, n_iter - 1 - it);   // tiles issued after this one
-    if constexpr (ST == 2) {
-      wait_barrier<0>();
-    } else if constexpr (ST == 3) {
-      if (ahead >= 1) wait_barrier<LPT>(); else wait_barrier<0>();
+      for (int u = 0; u < BPW; ++u) {
+        const int blk = w * BPW + u;
+        dma16_s(kt, koffs[u], kdst + blk * 1024);
+        dma16_s(vt, voffs[u], vdst + blk * 1024);
+      }
     } else {
-      if (ahead >= 2) wait_barrier<2 * LPT>();
-      else if (ahead == 1) wait_barrier<LPT>();
-      else wait_barrier<0>();
-    }
-    if (it + ST - 1 < n_iter) issue_tile(kb + (it + ST - 1) * KTILE, (it + ST - 1) % ST);
-
-    const int t0 = kb + it * KTILE;
-    const int g0 = t0 + kg * KT;
-    if (g0 >= ke) continue;
-    const unsigned char* sK = smem + (it % ST) * STAGE_B;
-    const unsigned char* sV = sK + TILE_B;
-
-    f32x16 s[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      s[mb] = f32x16{};
-      const int row = kg * KT + mb * 32 + lr;
-      const unsigned char* krow = sK + row * ROWB;
-      const int sw = swz<D>(row);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + hf) ^ sw) << 4));
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
+      for (int u = 0; u < BPW; ++u) {
+        const int blk = w * BPW + u;
+        const int row = blk * RPB + l_row;
+        const int c = l_slot ^ swz<D>(row);
+        const int j = min(t0 + row, ke - 1);
+        dma16(kptr + (int64_t)j * ks1 + c * 8, kdst + blk * 1024);
+        dma16(vptr + (int64_t)j * vs1 + c * 8, vdst + blk * 1024);
       }
     }
-    if (g0 + KT > ke) {
+  }
+};
+
+// Per-lane LDS byte offsets (within a stage) of the MFMA operands of a wave
+// whose keys start at row k0 of the tile.  Key-block and 16-key-step offsets
+// are multiples of 16 rows, leave the swizzle unchanged and go into the
+// instructions' immediate offsets (the 16-bit mask tells the compiler the
+// base is non-negative, which it needs before it folds a constant into a DS
+// offset).
+template <int D>
+struct OperandOffsets {
+  static constexpr int ROWB = D * 2;
+  unsigned kro[D / 16];     // K (A of S^T): row k0 + lr, chunk 2*ks + hf
+  unsigned vro[D / 32][2];  // V (A of O^T, transposed read)
+  __device__ __forceinline__ OperandOffsets(int k0, int lane) {
+    const int lr = lane & 31, hf = lane >> 5;
+    {
+      const int row = k0 + lr;
+      const int sw = swz<D>(row);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = g0 + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (key >= ke) s[mb][e] = -INFINITY;
-        }
+      for (int ks = 0; ks < D / 16; ++ks) kro[ks] = (unsigned)(row * ROWB + (((2 * ks + hf) ^ sw) << 4)) & 0xffffu;
     }
-    float mx = -INFINITY;
+    // 16-lane group tq covers dims db*32 + (tq%2)*16 .. +15; source lane ts
+    // addresses key row k0 + 4*hf + ts/4 (+8 for the upper half of a 16-key
+    // step), dims +4*(ts%4) .. +3, i.e. chunk 4db + 2(tq%2) + (ts%4)/2, half ts%2.
+    const int tq = lane >> 4, ts = lane & 15;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = pair_max(mx) * c2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = k0 + 8 * hi + 4 * hf + (ts >> 2);
+        const int c = 4 * db + 2 * (tq & 1) + ((ts & 3) >> 1);
+        vro[db][hi] = (unsigned)(row * ROWB + ((c ^ swz<D>(row)) << 4) + 8 * (ts & 1)) & 0xffffu;
+      }
+  }
+};
+
+// S^T (MB 32-key blocks) = K Q^T for the keys of one stage.
+template <int D, int MB>
+__device__ __forceinline__ void score_mfma(f32x16 (&s)[MB], const unsigned char* sK, const OperandOffsets<D>& off,
+                                           const bf16x8 (&qf)[D / 16]) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m_run = m_new;
+  for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off.kro[ks] + mb * 32 * (2 * D));
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
     }
-    float ps = 0.0f;
+}
+
+// O^T += V^T P^T for MB 32-key blocks; P packed as bf16, [block][16-key half].
+template <int D, int MB>
+__device__ __forceinline__ void pv_mfma(f32x16 (&o)[D / 32], const u32x4 (&pk)[MB][2], const unsigned char* sV,
+                                        const OperandOffsets<D>& off) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk[mb][h2]);
+      const int kofs = (mb * 32 + 16 * h2) * (2 * D);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(sV + off.vro[db][0] + kofs));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(sV + off.vro[db][1] + kofs));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+      }
+    }
+}
+
+// Online softmax of one tile's scores (MB blocks starting at key g0; keys at
+// or past ke are masked): moves the reference max if needed (rescaling O and
+// the running sum), turns the scores into P = 2^(s*c2 - m) in place, adds
+// them to the running sum and packs them as bf16 for P.V.
+template <int D, int MB>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[MB], u32x4 (&pk)[MB][2], f32x16 (&o)[D / 32], float& m_run,
+                                             float& l_run, float c2, int g0, int ke, int hf) {
+  if (g0 + MB * 32 > ke) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[mb][e], c2, -m_run));
-        s[mb][e] = pv;
-        ps += pv;
+        const int key = g0 + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (key >= ke) s[mb][e] = -INFINITY;
       }
-    l_run += ps;
-
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4 pw;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pw[q] = pack_bf16(s[mb][8 * h2 + 2 * q], s[mb][8 * h2 + 2 * q + 1]);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-        const int kbase16 = kg * KT + mb * 32 + 16 * h2;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int c = 4 * db + 2 * (tq & 1) + ((ts & 3) >> 1);
-          i16x4 lo, hi;
-          {
-            const int row = kbase16 + 4 * hf + (ts >> 2);
-            const unsigned char* a = sV + row * ROWB + ((c ^ swz<D>(row)) << 4) + 8 * (ts & 1);
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
-          }
-          {
-            const int row = kbase16 + 8 + 4 * hf + (ts >> 2);
-            const unsigned char* a = sV + row * ROWB + ((c ^ swz<D>(row)) << 4) + 8 * (ts & 1);
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
-          }
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-        }
-      }
-    }
   }
-
-  float l_tot = pair_sum(l_run);
-
-  if constexpr (KW > 1) {
-    wait_barrier<0>();
-    float* xs = reinterpret_cast<float*>(smem);
-    if (kg > 0) {
-      float* slot = xs + ((kg - 1) * RW + rw) * XSLOT;
+  const float mx = pair_max(tile_max(s)) * c2;
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+    const float m_new = vmax(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) slot[(db * 16 + e) * 64 + lane] = o[db][e];
-      slot[(DB * 16) * 64 + lane] = m_run;
-      slot[(DB * 16 + 1) * 64 + lane] = l_tot;
-    }
-    __syncthreads();
-    if (kg == 0) {
-      float mall = m_run;
-#pragma unroll
-      for (int q = 1; q < KW; ++q) mall = fmaxf(mall, xs[((q - 1) * RW + rw) * XSLOT + (DB * 16) * 64 + lane]);
-      if (mall != -INFINITY) {
-        const float a0 = __builtin_amdgcn_exp2f(m_run - mall);
-        l_tot *= a0;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= a0;
-#pragma unroll
-        for (int q = 1; q < KW; ++q) {
-          const float* slot = xs + ((q - 1) * RW + rw) * XSLOT;
-          const float aq = __builtin_amdgcn_exp2f(slot[(DB * 16) * 64 + lane] - mall);
-          l_tot += aq * slot[(DB * 16 + 1) * 64 + lane];
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[db][e] += aq * slot[(db * 16 + e) * 64 + lane];
-        }
-      }
-      m_run = mall;
-    }
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    m_run = m_new;
   }
+  float ps = 0.0f;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(s[mb][e], c2, -m_run));
+      s[mb][e] = pv;
+      ps += pv;
+    }
+  l_run += ps;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pk[mb][h2][q] = pack_bf16(s[mb][8 * h2 + 2 * q], s[mb][8 * h2 + 2 * q + 1]);
+}
 
-  bool writer = kg == 0 && rvalid;
-  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
+// Where one lane's query row lives and what it writes.
+struct RowOut {
+  int64_t orow;    // output row (packed row for varlen, b*max_q + i dense)
+  int64_t prow;    // dense row b*max_q + i (split partials are laid out dense)
+  int h;           // query head
+  int hf;          // lane half: dims 8j + 4*hf .. +3 of each 32-dim block
+  int split;
+};
+
+// Epilogue: normalises the accumulators and writes, by mode, the split
+// partial, the final prefix result, or the in-block result with the fused
+// log-space merge against the cached prefix result.
+template <int D, bool PREFETCH>
+__device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool writer, const RowOut& ro,
+                                             const f32x16 (&o)[D / 32], float m_run, float l_tot,
+                                             const f32x4* cache_a, float cache_l) {
+  constexpr int DB = D / 32;
+  const int hf = ro.hf;
   const bool has = l_tot > 0.0f;
   const float inv = has ? 1.0f / l_tot : 0.0f;
   const float L = has ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  const int64_t orow = varlen ? (int64_t)(qbase + i) : (int64_t)b * p.max_q + i;
-  const int64_t oe = orow * p.hq + h;
+  const int64_t oe = ro.orow * p.hq + ro.h;
 
   if (mode == kPrefixPartial) {
     // This split's partial result (normalised A and its L); the combine
     // kernel merges the splits.
     if (writer) {
       const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
-      const int64_t ve = (int64_t)split * n_entries + ((int64_t)b * p.max_q + i) * p.hq + h;
+      const int64_t ve = (int64_t)ro.split * n_entries + ro.prow * p.hq + ro.h;
       float* a = p.ws_a + ve * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -431,7 +393,7 @@ attn_bf16_kernel(const AttnParams p) {
   if (p.l && hf == 0) p.l[oe] = L;
   if (p.a_cache) {
     float lc;
-    if constexpr (kPrefetchCache) lc = cache_l; else lc = p.l_cache[oe];
+    if constexpr (PREFETCH) lc = cache_l; else lc = p.l_cache[oe];
     const float mm = fmaxf(lc, L);
     float wc = 0.0f, wi = 0.0f, lf = -INFINITY, rden = 0.0f;
     if (mm != -INFINITY) {
@@ -451,7 +413,7 @@ attn_bf16_kernel(const AttnParams p) {
         for (int j = 0; j < 4; ++j) {
           const int c0 = db * 32 + 8 * j + 4 * hf;
           f32x4 cv;
-          if constexpr (kPrefetchCache) cv = cache_a[db * 4 + j]; else cv = *reinterpret_cast<const f32x4*>(ac + c0);
+          if constexpr (PREFETCH) cv = cache_a[db * 4 + j]; else cv = *reinterpret_cast<const f32x4*>(ac + c0);
           f32x4 val;
 #pragma unroll
           for (int e = 0; e < 4; ++e) val[e] = fc * cv[e] + fi * o[db][4 * j + e];
@@ -462,6 +424,341 @@ attn_bf16_kernel(const AttnParams p) {
   }
 }
 
+// Work item of a workgroup covering ROWS query rows: (sequence, KV head,
+// row tile, key split) and the sequence's query/key ranges.
+struct Item {
+  int split, rt, b, kvh;
+  int qbase, nq, kbase, nk;
+  int row0, kb, ke, mode;
+  bool valid;
+};
+
+template <int ROWS>
+__device__ __forceinline__ Item decode_item(const AttnParams& p) {
+  Item it{};
+  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  it.valid = false;
+  if (item >= n_items) return it;
+  it.split = item % p.n_splits;
+  it.rt = (item / p.n_splits) % p.row_tiles;
+  const int bz = item / (p.n_splits * p.row_tiles);
+  it.b = bz / p.hkv;
+  it.kvh = bz - it.b * p.hkv;
+  it.qbase = 0;
+  it.nq = p.max_q;
+  it.kbase = 0;
+  it.nk = p.max_k;
+  if (p.cu_q != nullptr) {
+    it.qbase = p.cu_q[it.b];
+    it.nq = p.cu_q[it.b + 1] - it.qbase;
+    it.kbase = p.cu_k[it.b];
+    it.nk = p.cu_k[it.b + 1] - it.kbase;
+  }
+  const int R = p.group * it.nq;
+  it.row0 = it.rt * ROWS;
+  if (it.row0 >= R) return it;
+  it.kb = it.split * p.chunk;
+  // A sequence with no keys at all is finished by split 0 alone (A = 0,
+  // L = -inf); otherwise splits past the end have nothing to do.
+  it.mode = (p.mode == kPrefixPartial && it.nk == 0) ? kPrefixFinal : p.mode;
+  if (p.mode == kPrefixPartial && it.kb >= it.nk && !(it.nk == 0 && it.split == 0)) return it;
+  it.ke = min(it.nk, it.kb + p.chunk);
+  it.valid = true;
+  return it;
+}
+
+// True if some query head of rows [row0, row0+ROWS) needs its prefix
+// attention recomputed.
+template <int ROWS>
+__device__ __forceinline__ bool any_recompute(const AttnParams& p, const Item& it) {
+  const int R = p.group * it.nq;
+  const int rlast = min(R, it.row0 + ROWS) - 1;
+  bool any = false;
+  for (int g = it.row0 / it.nq; g <= rlast / it.nq; ++g) any |= p.decision[it.b * p.hq + it.kvh * p.group + g] == 0;
+  return any;
+}
+
+template <int D, int RW, int KW, int KT, int ST, bool GATED>
+__global__ void __launch_bounds__(64 * RW * KW)
+    __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
+attn_bf16_kernel(const AttnParams p) {
+  constexpr int NW = RW * KW;
+  constexpr int KTILE = KW * KT;                 // keys per iteration tile
+  using Dma = TileDma<D, NW, KTILE>;
+  constexpr int TILE_B = Dma::TILE_B;            // bytes of one K (or V) tile
+  constexpr int KS = D / 16;                     // MFMA k-steps over head dim
+  constexpr int DB = D / 32;                     // 32-dim output blocks
+  constexpr int MB = KT / 32;                    // 32-key blocks per key-wave
+  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int XSLOT = (DB * 16 + 2) * 64;      // floats per key-wave exchange slot
+  constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
+  constexpr int SMEM_R = ST * STAGE_B;
+  constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rw = w % RW, kg = w / RW;
+  const int lr = lane & 31, hf = lane >> 5;
+
+  const Item itm = decode_item<RW * 32>(p);
+  if (!itm.valid) return;
+  if constexpr (GATED) {
+    if (!any_recompute<RW * 32>(p, itm)) return;
+  }
+  const bool varlen = p.cu_q != nullptr;
+  const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
+  const int R = G * nq;
+
+  // --- this lane's query row and its Q operand (B of S^T = K Q^T) ---
+  const int r = itm.row0 + rw * 32 + lr;
+  const bool rvalid = r < R;
+  const int g = rvalid ? r / nq : 0;
+  const int i = rvalid ? r - g * nq : 0;
+  const int h = kvh * G + g;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+      (varlen ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
+      (int64_t)h * p.qs2;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = rvalid ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
+    qf[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
+      (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
+  const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
+      (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
+  const Dma dma(kptr, vptr, p.ks1, p.vs1, ke, w, lane);
+  auto issue_tile = [&](int t0, int st) {
+    const unsigned kdst = smem_base + st * STAGE_B;
+    dma.issue(t0, kdst, kdst + TILE_B);
+  };
+
+  // Single-wave workgroups serve small in-block problems, where the cache read
+  // of the merge would otherwise be one more memory round trip after the
+  // compute: fetch this lane's cached A_out/L_out now.
+  constexpr bool kPrefetchCache = (NW == 1);
+  f32x4 cache_a[kPrefetchCache ? 4 * DB : 1];
+  float cache_l = 0.0f;
+  if constexpr (kPrefetchCache) {
+    if (p.mode == kBlock && p.a_cache && rvalid) {
+      const int64_t ce = (varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i) * p.hq + h;
+      cache_l = p.l_cache[ce];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          cache_a[db * 4 + j] = *reinterpret_cast<const f32x4*>(p.a_cache + ce * D + db * 32 + 8 * j + 4 * hf);
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  const float c2 = p.scale_log2;
+  const OperandOffsets<D> off(kg * KT, lane);
+
+  auto compute_tile = [&](const unsigned char* sK, const unsigned char* sV, int g0) {
+    f32x16 s[MB];
+    u32x4 pk[MB][2];
+    score_mfma<D, MB>(s, sK, off, qf);
+    softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, g0, ke, hf);
+    pv_mfma<D, MB>(o, pk, sV, off);
+  };
+
+  const int n_iter = (ke > kb) ? (ke - kb + KTILE - 1) / KTILE : 0;
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < n_iter) issue_tile(kb + s * KTILE, s);
+
+  // The loop is unrolled over the ring so each copy reads a fixed stage.
+  for (int it0 = 0; it0 < n_iter; it0 += ST) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int it = it0 + st;
+      if (it < n_iter) {
+        const int ahead = min(ST - 2, n_iter - 1 - it);   // tiles issued after this one
+        if constexpr (ST == 2) {
+          wait_barrier<0>();
+        } else if constexpr (ST == 3) {
+          if (ahead >= 1) wait_barrier<Dma::OPS>(); else wait_barrier<0>();
+        } else {
+          if (ahead >= 2) wait_barrier<2 * Dma::OPS>();
+          else if (ahead == 1) wait_barrier<Dma::OPS>();
+          else wait_barrier<0>();
+        }
+        if (it + ST - 1 < n_iter) issue_tile(kb + (it + ST - 1) * KTILE, (st + ST - 1) % ST);
+        const int g0 = kb + it * KTILE + kg * KT;
+        if (g0 < ke) compute_tile(smem + st * STAGE_B, smem + st * STAGE_B + TILE_B, g0);
+      }
+    }
+  }
+
+  float l_tot = pair_sum(l_run);
+
+  if constexpr (KW > 1) {
+    wait_barrier<0>();
+    float* xs = reinterpret_cast<float*>(smem);
+    if (kg > 0) {
+      float* slot = xs + ((kg - 1) * RW + rw) * XSLOT;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) slot[(db * 16 + e) * 64 + lane] = o[db][e];
+      slot[(DB * 16) * 64 + lane] = m_run;
+      slot[(DB * 16 + 1) * 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (kg == 0) {
+      float mall = m_run;
+#pragma unroll
+      for (int q = 1; q < KW; ++q) mall = fmaxf(mall, xs[((q - 1) * RW + rw) * XSLOT + (DB * 16) * 64 + lane]);
+      if (mall != -INFINITY) {
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mall);
+        l_tot *= a0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= a0;
+#pragma unroll
+        for (int q = 1; q < KW; ++q) {
+          const float* slot = xs + ((q - 1) * RW + rw) * XSLOT;
+          const float aq = __builtin_amdgcn_exp2f(slot[(DB * 16) * 64 + lane] - mall);
+          l_tot += aq * slot[(DB * 16 + 1) * 64 + lane];
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] += aq * slot[(db * 16 + e) * 64 + lane];
+        }
+      }
+      m_run = mall;
+    }
+  }
+
+  bool writer = kg == 0 && rvalid;
+  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
+  const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
+                  itm.split};
+  write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
+}
+
+// Alternating-phase kernel: 8 waves, 256 query rows, 64-key tiles in an
+// NS-stage ring.  Group grp (waves 4*grp .. 4*grp+3, rows 128*grp .. +127)
+// alternates matrix phases (O += P(u-1) V(u-1), then S(u) = K(u) Q^T) and
+// vector phases (softmax of S(u) into P(u)), group 1 one phase behind group
+// 0, so at every workgroup phase one group is in its matrix phase and the
+// other in its vector phase; waves w and w+4 share a SIMD.  Every wave passes
+// the same 2n+2 barriers (n tiles).  Tile u is waited for at workgroup phase
+// 2u and last read (as V by group 1) in phase 2u+3, so its stage can take
+// tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
+// u+1 .. u+NS-3 may still be in flight.
+template <int D, int NS, bool GATED>
+__global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p) {
+  constexpr int NW = 8, ROWS = 256, KT = 64;
+  constexpr int LOOK = NS - 2;   // tiles issued ahead of the one waited for
+  static_assert(LOOK >= 1 && LOOK <= 3, "ring depth");
+  using Dma = TileDma<D, NW, KT>;
+  constexpr int TILE_B = Dma::TILE_B;
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int KS = D / 16, DB = D / 32, MB = KT / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE_B];
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = w >> 2;
+  const int lr = lane & 31, hf = lane >> 5;
+
+  const Item itm = decode_item<ROWS>(p);
+  if (!itm.valid) return;
+  if constexpr (GATED) {
+    if (!any_recompute<ROWS>(p, itm)) return;
+  }
+  const bool varlen = p.cu_q != nullptr;
+  const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
+  const int R = G * nq;
+
+  const int r = itm.row0 + w * 32 + lr;
+  const bool rvalid = r < R;
+  const bool active = itm.row0 + w * 32 < R;   // wave has some valid row
+  const int g = rvalid ? r / nq : 0;
+  const int i = rvalid ? r - g * nq : 0;
+  const int h = kvh * G + g;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+      (varlen ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
+      (int64_t)h * p.qs2;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = rvalid ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
+    qf[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
+      (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
+  const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
+      (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
+  const Dma dma(kptr, vptr, p.ks1, p.vs1, ke, w, lane);
+  auto issue_tile = [&](int u) {
+    const unsigned kdst = smem_base + (u % NS) * STAGE_B;
+    dma.issue(kb + u * KT, kdst, kdst + TILE_B);
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  const float c2 = p.scale_log2;
+  const OperandOffsets<D> off(0, lane);
+  f32x16 s[MB];
+  u32x4 pk[MB][2];
+
+  // Each wave runs the same phase sequence
+  //   M0: S(0) | V0: softmax(0) | M1: P.V(0), S(1) | V1 | ... | Mn: P.V(n-1)
+  // (2n+1 phases, each opened by a barrier); group 1 passes one extra
+  // barrier first and group 0 one extra at the end, so group 1 runs one
+  // phase behind.  At every even workgroup phase 2v all waves wait for tile
+  // v and issue tile v+2; for group 0 these are the barriers opening its
+  // matrix phases, for group 1 those opening its vector phases.
+  const int n = (ke > kb) ? (ke - kb + KT - 1) / KT : 0;
+  auto even_barrier = [&](int v) {
+    const int later = min(LOOK - 1, n - 1 - v);   // tiles issued after tile v
+    if (later >= 2) phase_barrier<2 * Dma::OPS>();
+    else if (later == 1) phase_barrier<Dma::OPS>();
+    else phase_barrier<0>();
+    if (v + LOOK < n) issue_tile(v + LOOK);
+  };
+#pragma unroll
+  for (int t = 0; t < LOOK; ++t)
+    if (t < n) issue_tile(t);
+  if (grp) even_barrier(0);
+  if (grp) phase_barrier<63>(); else even_barrier(0);
+  if (active && n > 0) score_mfma<D, MB>(s, smem, off, qf);
+  for (int u = 0; u < n; ++u) {
+    if (grp) even_barrier(u + 1); else phase_barrier<63>();
+    if (active) softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, kb + u * KT, ke, hf);
+    if (grp) phase_barrier<63>(); else even_barrier(u + 1);
+    if (active) {
+      pv_mfma<D, MB>(o, pk, smem + (u % NS) * STAGE_B + TILE_B, off);
+      if (u + 1 < n) score_mfma<D, MB>(s, smem + ((u + 1) % NS) * STAGE_B, off, qf);
+    }
+  }
+  if (!grp) phase_barrier<63>();
+
+  const float l_tot = pair_sum(l_run);
+  bool writer = rvalid;
+  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
+  const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
+                  itm.split};
+  write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
+}
 
 // N-way log-space merge of the split-KV partials (the merge equation applied
 // across key splits).  D/4 threads per (row, head) entry, four dims each; the
@@ -521,33 +818,62 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   if (t == 0) p.l[oo] = mx + __logf(den);
 }
 
-template <int D, int RW, int KW, int KT, int ST>
-hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
+hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
+  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  const int64_t epb = 256 / (d / 4);
+  const dim3 grid((unsigned)((n_entries + epb - 1) / epb));
+  if (d == 128)
+    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+dim3 item_grid(const AttnParams& p) {
   const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
   const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  dim3 grid(per_xcd * kXcds);
+  return dim3(per_xcd * kXcds);
+}
+
+template <int D, int RW, int KW, int KT, int ST>
+hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
+  const dim3 grid = item_grid(p);
   if (p.decision != nullptr && p.mode != kBlock)
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), grid, dim3(64 * RW * KW), 0, s, p);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), grid, dim3(64 * RW * KW), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.mode != kPrefixPartial) return err;
-  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
-  const int64_t epb = 256 / (D / 4);
-  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((n_entries + epb - 1) / epb)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_combine(p, D, s);
+}
+
+template <int D, int NS>
+hipError_t launch_pp(const AttnParams& p, hipStream_t s) {
+  const dim3 grid = item_grid(p);
+  if (p.decision != nullptr && p.mode != kBlock)
+    hipLaunchKernelGGL((attn_pp_kernel<D, NS, true>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_pp_kernel<D, NS, false>), grid, dim3(512), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.mode != kPrefixPartial) return err;
+  return launch_combine(p, D, s);
 }
 
 }  // namespace
 
-// Variants (rows per workgroup x keys per iteration tile, 2-stage ring):
-//   0: 128 rows (4 row-waves) x 64 keys (64 KB LDS at d=128: 2 WG per CU)
+// Variants (rows per workgroup x keys per iteration tile):
+//   0: 128 rows (4 row-waves) x 64 keys, 2-stage ring (64 KB LDS at d=128:
+//      2 WG per CU)
 //   1:  64 rows (2 row-waves x 2 key-waves of 32) x 64 keys (2 WG per CU);
 //       also used for fewer rows: the streaming, not the MFMA, sets the pace
 //   2:  32 rows x 32 keys, one wave (8 KB LDS at d=128): small in-block
 //       problems, where latency dominates
+//   3: 256 rows (two alternating groups of 4 waves) x 64 keys, 4-stage ring
+//      (128 KB LDS at d=128: 1 WG per CU): many rows per KV head, where the
+//      matrix cores set the pace
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
   (void)d;
+  if (prefix && rows_per_kv_head > 192) return Bf16Plan{3, 256, 64, 1};
   if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64, 2};
   if (rows_per_kv_head <= 32 && max_k <= 64 && !prefix) return Bf16Plan{2, 32, 32, 8};
   return Bf16Plan{1, 64, 64, 2};
@@ -564,12 +890,14 @@ hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hi
     switch (plan.variant) {
       case 0: return launch_variant<128, 4, 1, 64, 2>(p, s);
       case 1: return launch_variant<128, 2, 2, 32, 2>(p, s);
+      case 3: return launch_pp<128, 4>(p, s);
       default: return launch_variant<128, 1, 1, 32, 2>(p, s);
     }
   }
   switch (plan.variant) {
     case 0: return launch_variant<64, 4, 1, 64, 2>(p, s);
     case 1: return launch_variant<64, 2, 2, 32, 2>(p, s);
+    case 3: return launch_pp<64, 4>(p, s);
     default: return launch_variant<64, 1, 1, 32, 2>(p, s);
   }
 }

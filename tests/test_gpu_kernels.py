@@ -233,6 +233,15 @@ DENSE_SHAPES = [
     (1, 4, 4, 128, 64, 32),     # exactly one tile, one split
     (2, 6, 3, 64, 555, 41),     # head dim 64
     (1, 3, 1, 64, 129, 9),      # G = 3, 27 rows
+    # 256-row alternating kernel: 200 rows (wave 7 idle, wave 6 ragged),
+    # one 64-key tile per split with a ragged last split
+    (1, 8, 2, 128, 1000, 50),
+    # 520 rows: the last row tile has 8 rows (group 1 idle), 6 tiles
+    (2, 4, 1, 128, 333, 130),
+    # head dim 64, 300 rows
+    (1, 2, 2, 64, 700, 300),
+    # few splits of many tiles each: the 4-stage ring wraps several times
+    (4, 16, 16, 128, 3000, 200),
 ]
 
 
@@ -259,8 +268,10 @@ def test_prefix_attn(dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefix_attn_decision_leaves_cache_untouched(dtype):
-    B, hq, hkv, d, lp, nb = 3, 6, 2, 128, 900, 33
+@pytest.mark.parametrize("shape", [(3, 6, 2, 128, 900, 33), (3, 8, 2, 128, 700, 70)])
+def test_prefix_attn_decision_leaves_cache_untouched(dtype, shape):
+    # the second shape (280 rows per KV head) runs the 256-row kernel
+    B, hq, hkv, d, lp, nb = shape
     s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=61)
     want_a, want_l = _oracle_prefix(s)
     r = np.random.default_rng(3)
@@ -285,12 +296,14 @@ def test_prefix_attn_decision_leaves_cache_untouched(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefix_attn_empty_prefix(dtype):
-    s = _dense_inputs(dtype, 2, 4, 2, 128, 0, 20, seed=62)
+@pytest.mark.parametrize("nb", [20, 150])
+def test_prefix_attn_empty_prefix(dtype, nb):
+    # nb = 150: 300 rows per KV head, the 256-row kernel
+    s = _dense_inputs(dtype, 2, 4, 2, 128, 0, nb, seed=62)
     q = dev_in(s.q[0], dtype)
     kp = torch.zeros(2, 2, 0, 128, device=DEV, dtype=q.dtype)
-    a = torch.full((40, 4, 128), 5.0, device=DEV)
-    l = torch.full((40, 4), 5.0, device=DEV)
+    a = torch.full((2 * nb, 4, 128), 5.0, device=DEV)
+    l = torch.full((2 * nb, 4), 5.0, device=DEV)
     assert ba.ba_prefix_attn_workspace(q, kp, kp) == 0
     ba.ba_prefix_attn(q, kp, kp, a, l)
     torch.cuda.synchronize()
