@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     ba_block_attn,
     ba_lse_merge,
     ba_prefix_attn,
+    ba_prefix_attn_merge,
     ba_prefix_attn_workspace,
     ba_reuse_gate,
     ba_reuse_gate_workspace,

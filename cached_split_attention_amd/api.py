@@ -137,6 +137,25 @@ def ba_prefix_attn(q, k, v, a_out, l_out, workspace=None, *, q_layout="bshd", kv
                                _stream(stream)))
 
 
+def ba_prefix_attn_merge(q, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None, workspace=None, *,
+                         q_layout="bshd", kv_layout="bhsd", cu_q=None, cu_k=None, max_q=None, max_k=None,
+                         decision=None, scale=None, stream=None):
+    """ba_prefix_attn, then A_full/L_full = merge(A_out/L_out, A_in/L_in) for every row and head
+    (A_out/L_out fresh, or cached for heads whose decision is 1)."""
+    desc, rows = _desc(q, k, v, q_layout=q_layout, kv_layout=kv_layout, cu_q=cu_q, cu_k=cu_k,
+                       max_q=max_q, max_k=max_k, scale=scale, decision=decision)
+    for t, nm in ((a_out, "a_out"), (a_in, "a_in"), (a_full, "a_full")):
+        _check_out(t, (rows, desc.hq, desc.d), torch.float32, nm)
+    for t, nm in ((l_out, "l_out"), (l_in, "l_in")):
+        _check_out(t, (rows, desc.hq), torch.float32, nm)
+    if l_full is not None:
+        _check_out(l_full, (rows, desc.hq), torch.float32, "l_full")
+    _need_gpu(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().ba_prefix_attn_merge(ctypes.byref(desc), _ptr(a_out), _ptr(l_out), _ptr(a_in), _ptr(l_in),
+                                     _ptr(a_full), _ptr(l_full), _ptr(workspace), nbytes, _stream(stream)))
+
+
 def ba_block_attn(q, k, v, *, a_cache=None, l_cache=None, a_in=None, l_in=None, a_full=None,
                   l_full=None, q_layout="bshd", kv_layout="bshd", cu_q=None, cu_k=None, max_q=None,
                   max_k=None, scale=None, stream=None):

@@ -110,10 +110,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
 }
 
-// As dma16, from a wave-uniform base plus a per-lane 32-bit byte offset.
+// As dma16, from a wave-uniform base plus a per-lane 32-bit byte offset (the
+// base is read from the first lane, so it lives in scalar registers).
 __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(base) : "memory");
+  // (readfirstlane returns int: each half goes through unsigned, so the low
+  // half is zero-extended, not sign-extended, into the 64-bit address)
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const uint64_t su = lo | (hi << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "s"(base) : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight,
@@ -761,9 +768,16 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p) {
 }
 
 // N-way log-space merge of the split-KV partials (the merge equation applied
-// across key splits).  D/4 threads per (row, head) entry, four dims each; the
-// L and A partials of up to 8 splits are loaded together, so one memory
-// round trip serves a batch.
+// across key splits), optionally followed by the merge with a precomputed
+// in-block part.  D/4 threads per (row, head) entry, four dims each.
+//   p.mode == kPrefixPartial: entries whose prefix was recomputed combine the
+//     split partials into A_out/L_out (p.a, p.l); the L and A partials of up
+//     to 8 splits are loaded together, so one memory round trip serves a
+//     batch.  Entries of reused heads (or of sequences with no prefix keys)
+//     keep the A_out/L_out already in p.a/p.l.
+//   p.mode == kPrefixFinal: A_out/L_out are already in p.a/p.l.
+//   p.a_full != NULL: A_full/L_full = merge(A_out, L_out, A_in, L_in) with
+//     A_in/L_in in p.a_cache/p.l_cache, for every entry.
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   constexpr int TPE = D / 4;
@@ -782,41 +796,71 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     nq = p.cu_q[b + 1] - qbase;
     nk = p.cu_k[b + 1] - p.cu_k[b];
   }
-  if (i >= nq || nk == 0) return;  // empty prefix: written by the attention kernel
-  if (p.decision && p.decision[b * p.hq + h]) return;
-  const int ns = (nk + p.chunk - 1) / p.chunk;
-  const float* la = p.ws_l + e;
-  const float* aa = p.ws_a + e * D + 4 * t;
-  const int64_t cs = n_entries;
-  float mx = -INFINITY, den = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c0 = 0; c0 < ns; c0 += 8) {
-    float lv[8];
-    f32x4 av[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = c0 + u < ns;
-      lv[u] = ok ? la[(c0 + u) * cs] : -INFINITY;
-      av[u] = ok ? *reinterpret_cast<const f32x4*>(aa + (c0 + u) * cs * D) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    float bm = mx;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) bm = fmaxf(bm, lv[u]);
-    const float r = __builtin_amdgcn_exp2f((mx - bm) * kLog2e);  // rescale earlier batches
-    den *= r;
-    acc *= r;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wgt = __builtin_amdgcn_exp2f((lv[u] - bm) * kLog2e);
-      den += wgt;
-      acc += wgt * av[u];
-    }
-    mx = bm;
-  }
+  if (i >= nq) return;
   const int64_t oo = (p.cu_q ? (int64_t)(qbase + i) : vrow) * p.hq + h;
-  *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t) = acc * (1.0f / den);
-  if (t == 0) p.l[oo] = mx + __logf(den);
+  // An empty prefix is written by the attention kernel's split 0.
+  const bool fresh = p.mode == kPrefixPartial && nk > 0 && !(p.decision && p.decision[b * p.hq + h]);
+  if (!fresh && !p.a_full) return;
+  f32x4 a_o;
+  float l_o;
+  if (fresh) {
+    const int ns = (nk + p.chunk - 1) / p.chunk;
+    const float* la = p.ws_l + e;
+    const float* aa = p.ws_a + e * D + 4 * t;
+    const int64_t cs = n_entries;
+    float mx = -INFINITY, den = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < ns; c0 += 8) {
+      float lv[8];
+      f32x4 av[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = c0 + u < ns;
+        lv[u] = ok ? la[(c0 + u) * cs] : -INFINITY;
+        av[u] = ok ? *reinterpret_cast<const f32x4*>(aa + (c0 + u) * cs * D) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      float bm = mx;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) bm = fmaxf(bm, lv[u]);
+      const float r = __builtin_amdgcn_exp2f((mx - bm) * kLog2e);  // rescale earlier batches
+      den *= r;
+      acc *= r;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = __builtin_amdgcn_exp2f((lv[u] - bm) * kLog2e);
+        den += wgt;
+        acc += wgt * av[u];
+      }
+      mx = bm;
+    }
+    a_o = acc * (1.0f / den);
+    l_o = mx + __logf(den);
+    *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t) = a_o;
+    if (t == 0) p.l[oo] = l_o;
+  } else {
+    a_o = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
+    l_o = p.l[oo];
+  }
+  if (p.a_full) {
+    const float li = p.l_cache[oo];
+    const f32x4 ai = *reinterpret_cast<const f32x4*>(p.a_cache + oo * D + 4 * t);
+    const float mm = fmaxf(l_o, li);
+    f32x4 af = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lf = -INFINITY;
+    if (mm != -INFINITY) {
+      const float wo = __builtin_amdgcn_exp2f((l_o - mm) * kLog2e);
+      const float wi = __builtin_amdgcn_exp2f((li - mm) * kLog2e);
+      const float den = wo + wi;
+      const float rden = 1.0f / den;
+      af = (wo * rden) * a_o + (wi * rden) * ai;
+      lf = mm + __logf(den);
+    }
+    *reinterpret_cast<f32x4*>(p.a_full + oo * D + 4 * t) = af;
+    if (t == 0 && p.l_full) p.l_full[oo] = lf;
+  }
 }
+
+}  // namespace
 
 hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
   const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
@@ -828,6 +872,8 @@ hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
+
+namespace {
 
 dim3 item_grid(const AttnParams& p) {
   const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
@@ -842,9 +888,7 @@ hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), grid, dim3(64 * RW * KW), 0, s, p);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), grid, dim3(64 * RW * KW), 0, s, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.mode != kPrefixPartial) return err;
-  return launch_combine(p, D, s);
+  return hipGetLastError();
 }
 
 template <int D, int NS>
@@ -854,9 +898,7 @@ hipError_t launch_pp(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_pp_kernel<D, NS, true>), grid, dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((attn_pp_kernel<D, NS, false>), grid, dim3(512), 0, s, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.mode != kPrefixPartial) return err;
-  return launch_combine(p, D, s);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -885,7 +927,9 @@ int max_splits_bf16(int d, int variant) {
   return 256;
 }
 
-hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s) {
+hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, int d, hipStream_t s) {
+  Bf16Plan plan = plan_in;
+  if (plan.variant == 2 && p.mode != kBlock) plan.variant = 1;  // single-wave shape: in-block only
   if (d == 128) {
     switch (plan.variant) {
       case 0: return launch_variant<128, 4, 1, 64, 2>(p, s);

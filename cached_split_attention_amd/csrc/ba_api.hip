@@ -131,6 +131,8 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
 }
 
 // Workspace: [partial A f32 [splits][entries][d]][partial L f32 [splits][entries]].
+// Workspace of a split plan: partial A [splits][entries][d] f32, then
+// partial L [splits][entries] f32.
 size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
   if (pp.n_splits <= 1) return 0;
   const size_t entries = (size_t)d->n_seq * d->max_q * d->hq;
@@ -177,14 +179,23 @@ size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   return prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
 }
 
-ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
+namespace {
+
+// Prefix attention, optionally followed by the merge with a precomputed
+// in-block part (a_in != NULL).
+ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
+                      const float* l_in, float* a_full, float* l_full, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
   if (desc->n_seq == 0 || desc->max_q == 0) return BA_OK;
   if (!a_out || !l_out) return fail(BA_ERR_NULL, "a_out and l_out are required");
+  const bool merge = a_in != nullptr || l_in != nullptr || a_full != nullptr || l_full != nullptr;
+  if (merge && (!a_in || !l_in || !a_full))
+    return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
+  if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
+    return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
   const PrefixPlan pp = plan_prefix(desc, sh.group);
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -196,25 +207,48 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
   p.chunk = pp.chunk;
   p.n_splits = pp.n_splits;
   p.row_tiles = pp.row_tiles;
-  if (desc->dtype == BA_F32) {
-    p.mode = ba::kPrefixFinal;
-    p.a = a_out;
-    p.l = l_out;
-    return hip_status(ba::launch_attn_f32(p, desc->d, stream), "prefix attention (f32)");
-  }
-  if (pp.n_splits == 1) {
-    p.mode = ba::kPrefixFinal;
-    p.a = a_out;
-    p.l = l_out;
-    return hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention");
-  }
-  const size_t entries = (size_t)desc->n_seq * desc->max_q * desc->hq;
-  p.mode = ba::kPrefixPartial;
   p.a = a_out;
   p.l = l_out;
-  p.ws_a = static_cast<float*>(workspace);
-  p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
-  return hip_status(ba::launch_attn_bf16(pp.bf, p, desc->d, stream), "prefix attention (split)");
+  hipError_t err;
+  if (desc->dtype == BA_F32 || pp.n_splits == 1) {
+    p.mode = ba::kPrefixFinal;
+  } else {
+    const size_t entries = (size_t)desc->n_seq * desc->max_q * desc->hq;
+    p.mode = ba::kPrefixPartial;
+    p.ws_a = static_cast<float*>(workspace);
+    p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
+  }
+  err = desc->dtype == BA_F32 ? ba::launch_attn_f32(p, desc->d, stream)
+                              : ba::launch_attn_bf16(pp.bf, p, desc->d, stream);
+  if (err != hipSuccess) return hip_status(err, "prefix attention");
+  if (p.mode != ba::kPrefixPartial && !merge) return BA_OK;
+  // One pass combines the split partials across many workgroups (the
+  // combine needs the whole chip's bandwidth, not one workgroup's) and, when
+  // asked, merges A_out/L_out (fresh, or cached for reused heads) with
+  // A_in/L_in into A_full/L_full.
+  if (merge) {
+    p.a_cache = a_in;
+    p.l_cache = l_in;
+    p.a_full = a_full;
+    p.l_full = l_full;
+  }
+  return hip_status(ba::launch_combine(p, desc->d, stream), merge ? "prefix merge" : "split combine");
+}
+
+}  // namespace
+
+ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
+                               const float* l_in, float* a_full, float* l_full, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!a_in || !l_in || !a_full) return fail(BA_ERR_NULL, "a_in, l_in and a_full are required");
+  return prefix_impl(desc, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream);
 }
 
 ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache, float* a_in,

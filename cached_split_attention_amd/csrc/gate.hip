@@ -31,22 +31,58 @@ __device__ __forceinline__ void st_agent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Does row (b, pos, head) differ between cur and prev?  W = comparison word.
 template <typename W>
-__device__ bool rows_differ(const void* cur, const void* prev, int64_t s0, int64_t s1, int64_t s2,
-                            int b, int pos, int heads, int row_bytes, int esize) {
-  const int wpr = row_bytes / (int)sizeof(W);
+__device__ __forceinline__ bool words_differ(const W& x, const W& y) {
+  if constexpr (sizeof(W) == 16) {
+    return (x[0] != y[0]) | (x[1] != y[1]) | (x[2] != y[2]) | (x[3] != y[3]);
+  } else {
+    return x != y;
+  }
+}
+
+// Does any Q, K or V row of block position (b, pos) differ between cur and
+// prev?  The position's words (Q heads, then K heads, then V heads; W = the
+// comparison word) are spread over the workgroup, 8 per thread per round,
+// with all of a round's loads issued before any comparison so a round costs
+// one memory latency.
+template <typename W>
+__device__ bool position_changed(const GateParams& p, int b, int pos) {
+  const int wpr = p.d * p.esize / (int)sizeof(W);
+  const int nq = p.hq * wpr;
+  const int nk = p.k_cur ? p.hkv * wpr : 0;
+  const int nv = p.v_cur ? p.hkv * wpr : 0;
+  const int total = nq + nk + nv;
+  constexpr int U = 8;
   bool diff = false;
-  for (int t = threadIdx.x; t < heads * wpr; t += blockDim.x) {
-    const int hh = t / wpr, wi = t - hh * wpr;
-    const int64_t off = ((int64_t)b * s0 + (int64_t)pos * s1 + (int64_t)hh * s2) * esize;
-    const W x = reinterpret_cast<const W*>(static_cast<const char*>(cur) + off)[wi];
-    const W y = reinterpret_cast<const W*>(static_cast<const char*>(prev) + off)[wi];
-    if constexpr (sizeof(W) == 16) {
-      diff |= (x[0] != y[0]) | (x[1] != y[1]) | (x[2] != y[2]) | (x[3] != y[3]);
-    } else {
-      diff |= x != y;
+  for (int t0 = threadIdx.x; t0 < total; t0 += U * (int)blockDim.x) {
+    W x[U], y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int w = t0 + u * (int)blockDim.x;
+      x[u] = W{};
+      y[u] = W{};
+      if (w < total) {
+        const void* cur = p.q_cur;
+        const void* prev = p.q_prev;
+        int64_t s0 = p.qs0, s1 = p.qs1, s2 = p.qs2;
+        if (w >= nq) {
+          w -= nq;
+          const bool isv = w >= nk;
+          if (isv) w -= nk;
+          cur = isv ? p.v_cur : p.k_cur;
+          prev = isv ? p.v_prev : p.k_prev;
+          s0 = p.ks0;
+          s1 = p.ks1;
+          s2 = p.ks2;
+        }
+        const int hh = w / wpr, wi = w - hh * wpr;
+        const int64_t off = ((int64_t)b * s0 + (int64_t)pos * s1 + (int64_t)hh * s2) * p.esize;
+        x[u] = reinterpret_cast<const W*>(static_cast<const char*>(cur) + off)[wi];
+        y[u] = reinterpret_cast<const W*>(static_cast<const char*>(prev) + off)[wi];
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) diff |= words_differ(x[u], y[u]);
   }
   return diff;
 }
@@ -58,10 +94,7 @@ __global__ void __launch_bounds__(256) gate_count_kernel(const GateParams p) {
   if (p.upd_mask) {
     diff = threadIdx.x == 0 && p.upd_mask[(int64_t)b * p.n_blk + pos] != 0;
   } else {
-    const int rb = p.d * p.esize;
-    diff = rows_differ<W>(p.q_cur, p.q_prev, p.qs0, p.qs1, p.qs2, b, pos, p.hq, rb, p.esize);
-    if (p.k_cur) diff |= rows_differ<W>(p.k_cur, p.k_prev, p.ks0, p.ks1, p.ks2, b, pos, p.hkv, rb, p.esize);
-    if (p.v_cur) diff |= rows_differ<W>(p.v_cur, p.v_prev, p.ks0, p.ks1, p.ks2, b, pos, p.hkv, rb, p.esize);
+    diff = position_changed<W>(p, b, pos);
   }
   diff = __syncthreads_or(diff);
   // One atomic per workgroup carries both the ticket (low 16 bits) and the

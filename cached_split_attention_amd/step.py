@@ -4,17 +4,21 @@ FlashBlock (gist.science/es/paper/2602.05305), section 2: each step runs the
 reuse gate, recomputes the out-of-block part (A_out, L_out) only for the
 (sequence, head) pairs the gate sends to recompute (the kernel itself skips
 the others, reading the decision from device memory, so there is no
-device-to-host synchronisation), then computes the in-block part and merges
-it with the cache in one fused kernel.  The cache stays valid until the next
-block starts.  This module only orders calls and owns buffers; it computes
-nothing itself.
+device-to-host synchronisation), and merges it with the in-block part.  The
+in-block part (A_in, L_in) depends on neither the gate nor the cache, so it
+runs first; the prefix call then merges A_out/L_out (fresh or cached) with
+it in its last pass, so a step is three launches on one stream (a second
+stream would let the in-block part overlap the gate, but a cross-stream
+dependency inside a replayed graph costs far more than the overlap saves).
+The cache stays valid until the next block starts.  This module only orders
+calls and owns buffers; it computes nothing itself.
 """
 
 from __future__ import annotations
 
 import torch
 
-from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_block_attn, ba_prefix_attn,
+from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_block_attn, ba_prefix_attn_merge,
                   ba_prefix_attn_workspace, ba_reuse_gate, ba_reuse_gate_workspace)
 
 
@@ -41,6 +45,8 @@ class CachedBlockAttention:
         self.l_out = torch.zeros(rows, hq, device=dev, dtype=torch.float32)
         self.a_full = torch.empty(rows, hq, self.d, device=dev, dtype=torch.float32)
         self.l_full = torch.empty(rows, hq, device=dev, dtype=torch.float32)
+        self.a_in = torch.empty(rows, hq, self.d, device=dev, dtype=torch.float32)
+        self.l_in = torch.empty(rows, hq, device=dev, dtype=torch.float32)
         self.decision = torch.zeros(self.B, hq, device=dev, dtype=torch.uint8)
         self.m_count = torch.zeros(self.B, device=dev, dtype=torch.int32)
         self.cos = torch.zeros(self.B, hq, device=dev, dtype=torch.float64)
@@ -73,22 +79,23 @@ class CachedBlockAttention:
         prefix_events: optional (start, end) events recorded around the
         prefix pass on the launch stream."""
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        ba_block_attn(q, k, v, a_in=self.a_in, l_in=self.l_in, scale=self.scale, stream=main)
         if self.mode == BA_GATE_COUNT:
             ba_reuse_gate(self.mode, q, q_prev, k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev,
                           tau=self.tau, cache_valid=self.cache_valid, m_count=self.m_count,
-                          decision=self.decision, workspace=self._gws, stream=stream)
+                          decision=self.decision, workspace=self._gws, stream=main)
         else:
             ba_reuse_gate(self.mode, q, q_prev, gamma=self.gamma, cache_valid=self.cache_valid,
-                          cos=self.cos, decision=self.decision, workspace=self._gws, stream=stream)
+                          cos=self.cos, decision=self.decision, workspace=self._gws, stream=main)
         if prefix_events is not None:
-            prefix_events[0].record(stream)
-        ba_prefix_attn(q, self.kp, self.vp, self.a_out, self.l_out, self._ws, kv_layout=self.kv_layout,
-                       decision=self.decision if self.cache_valid else None, scale=self.scale,
-                       stream=stream)
+            prefix_events[0].record(main)
+        ba_prefix_attn_merge(q, self.kp, self.vp, self.a_out, self.l_out, self.a_in, self.l_in,
+                             self.a_full, self.l_full, self._ws, kv_layout=self.kv_layout,
+                             decision=self.decision if self.cache_valid else None, scale=self.scale,
+                             stream=main)
         if prefix_events is not None:
-            prefix_events[1].record(stream)
-        ba_block_attn(q, k, v, a_cache=self.a_out, l_cache=self.l_out, a_full=self.a_full,
-                      l_full=self.l_full, scale=self.scale, stream=stream)
+            prefix_events[1].record(main)
         self.cache_valid = True
         return self.a_full, self.l_full
 

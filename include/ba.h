@@ -112,6 +112,24 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Prefix attention fused with the log-space merge of FlashBlock "Mecanismo
+ * Central", for a step that computes the in-block part first (for example
+ * ba_block_attn with a_in/l_in outputs, concurrently with the reuse gate):
+ * exactly ba_prefix_attn, and then for every (row, query head)
+ *   A_full, L_full = merge(A_out, L_out, A_in, L_in)
+ * by the equation in this header's preamble, where A_out/L_out are the values
+ * just computed or, for (sequence, head) pairs whose decision is 1, the
+ * cached ones already in a_out/l_out.  a_in/l_in and a_full/l_full are
+ * float32 [R, hq, d] / [R, hq] with R as for a_out (rows past a sequence's
+ * length in varlen mode are not touched); l_full may be NULL.  The
+ * workspace is the one ba_prefix_attn_workspace() sizes for the same
+ * descriptor.  Errors as for ba_prefix_attn; a_in, l_in, a_full are required.
+ */
+ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_out,
+                               const float* a_in, const float* l_in, float* a_full, float* l_full,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * In-block attention with the fused log-space merge, FlashBlock "Mecanismo
  * Central": every query row attends over all of its sequence's block keys
  * with no mask (the block is bidirectional), giving A_in / L_in.  If a_cache

@@ -296,6 +296,64 @@ def test_prefix_attn_decision_leaves_cache_untouched(dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 6, 2, 128, 900, 33), (1, 4, 4, 128, 64, 32), (3, 8, 2, 128, 700, 70),
+                                   (2, 6, 3, 64, 555, 41), (2, 4, 2, 128, 0, 20)])
+def test_prefix_attn_merge(dtype, shape):
+    # Prefix pass fused with the merge against a precomputed in-block part:
+    # recomputed heads merge fresh A_out/L_out, reused heads the cached ones
+    # (left untouched); split and single-pass plans, the 256-row kernel, d=64
+    # and an empty prefix.
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=71)
+    rows = B * nb
+    if lp > 0:
+        want_a, want_l = _oracle_prefix(s)
+    else:
+        want_a, want_l = np.zeros((rows, hq, d)), np.full((rows, hq), -np.inf)
+    r = np.random.default_rng(9)
+    a_in = r.standard_normal((rows, hq, d)).astype(np.float32)
+    l_in = (r.standard_normal((rows, hq)) * 3 + 2).astype(np.float32)
+    l_in[::7, 0] = -np.inf
+    a_in[::7, 0] = 0.0
+    cache_a = r.standard_normal((rows, hq, d)).astype(np.float32)
+    cache_l = r.standard_normal((rows, hq)).astype(np.float32)
+    dec = (r.random((B, hq)) < 0.5).astype(np.uint8)
+    dec[0, 0] = 0
+    exp_a, exp_l = want_a.copy(), want_l.copy()
+    for b in range(B):
+        for h in range(hq):
+            if dec[b, h]:
+                exp_a[b * nb:(b + 1) * nb, h] = cache_a[b * nb:(b + 1) * nb, h]
+                exp_l[b * nb:(b + 1) * nb, h] = cache_l[b * nb:(b + 1) * nb, h]
+    want_f, want_lf = oracle.merge(exp_a, exp_l, a_in, l_in)
+    q = dev_in(s.q[0], dtype)
+    if lp > 0:
+        kp, vp = dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    else:
+        kp = vp = torch.zeros(B, hkv, 0, d, device=DEV, dtype=q.dtype)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    a_out = torch.from_numpy(cache_a).to(DEV)
+    l_out = torch.from_numpy(cache_l).to(DEV)
+    a_full = torch.full((rows, hq, d), 5.0, device=DEV)
+    l_full = torch.full((rows, hq), 5.0, device=DEV)
+    ba.ba_prefix_attn_merge(q, kp, vp, a_out, l_out, torch.from_numpy(a_in).to(DEV),
+                            torch.from_numpy(l_in).to(DEV), a_full, l_full, ws,
+                            decision=torch.from_numpy(dec).to(DEV))
+    torch.cuda.synchronize()
+    ga, gl = host(a_out), host(l_out)
+    for b in range(B):
+        for h in range(hq):
+            sl = slice(b * nb, (b + 1) * nb)
+            if dec[b, h]:
+                assert np.array_equal(ga[sl, h], cache_a[sl, h]) and np.array_equal(gl[sl, h], cache_l[sl, h])
+            else:
+                check_a(ga[sl, h], want_a[sl, h], f"A_out b{b} h{h}")
+                check_l(gl[sl, h], want_l[sl, h], f"L_out b{b} h{h}")
+    check_a(host(a_full), want_f, "A_full")
+    check_l(host(l_full), want_lf, "L_full")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("nb", [20, 150])
 def test_prefix_attn_empty_prefix(dtype, nb):
     # nb = 150: 300 rows per KV head, the 256-row kernel
