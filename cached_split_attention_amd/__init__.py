@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     ba_prefix_attn_workspace,
     ba_reuse_gate,
     ba_reuse_gate_workspace,
+    ba_split_attn,
     ba_varlen_pack,
     ba_version,
 )

@@ -156,6 +156,28 @@ def ba_prefix_attn_merge(q, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None,
                                      _ptr(a_full), _ptr(l_full), _ptr(workspace), nbytes, _stream(stream)))
 
 
+def ba_split_attn(q, kp, vp, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None, workspace=None, *,
+                  q_layout="bshd", kv_layout="bhsd", block_kv_layout="bshd", cu_q=None, cu_kp=None,
+                  cu_k=None, max_q=None, max_kp=None, max_k=None, decision=None, scale=None, stream=None):
+    """Prefix part (kp, vp; gated by decision) and in-block part (k, v) in one launch, then the
+    split combine and the merge into a_full/l_full."""
+    dp, rows = _desc(q, kp, vp, q_layout=q_layout, kv_layout=kv_layout, cu_q=cu_q, cu_k=cu_kp,
+                     max_q=max_q, max_k=max_kp, scale=scale, decision=decision)
+    db, _ = _desc(q, k, v, q_layout=q_layout, kv_layout=block_kv_layout, cu_q=cu_q, cu_k=cu_k,
+                  max_q=max_q, max_k=max_k, scale=scale, decision=None)
+    for t, nm in ((a_out, "a_out"), (a_in, "a_in"), (a_full, "a_full")):
+        _check_out(t, (rows, dp.hq, dp.d), torch.float32, nm)
+    for t, nm in ((l_out, "l_out"), (l_in, "l_in")):
+        _check_out(t, (rows, dp.hq), torch.float32, nm)
+    if l_full is not None:
+        _check_out(l_full, (rows, dp.hq), torch.float32, "l_full")
+    _need_gpu(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().ba_split_attn(ctypes.byref(dp), ctypes.byref(db), _ptr(a_out), _ptr(l_out), _ptr(a_in),
+                              _ptr(l_in), _ptr(a_full), _ptr(l_full), _ptr(workspace), nbytes,
+                              _stream(stream)))
+
+
 def ba_block_attn(q, k, v, *, a_cache=None, l_cache=None, a_in=None, l_in=None, a_full=None,
                   l_full=None, q_layout="bshd", kv_layout="bshd", cu_q=None, cu_k=None, max_q=None,
                   max_k=None, scale=None, stream=None):

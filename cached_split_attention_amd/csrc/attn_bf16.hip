@@ -441,11 +441,11 @@ struct Item {
 };
 
 template <int ROWS>
-__device__ __forceinline__ Item decode_item(const AttnParams& p) {
+__device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   Item it{};
   const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
   const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int item = (wg % kXcds) * per_xcd + wg / kXcds;
   it.valid = false;
   if (item >= n_items) return it;
   it.split = item % p.n_splits;
@@ -487,10 +487,16 @@ __device__ __forceinline__ bool any_recompute(const AttnParams& p, const Item& i
   return any;
 }
 
-template <int D, int RW, int KW, int KT, int ST, bool GATED>
+// A launch may carry two independent parts (the prefix and the in-block
+// attention of one step): workgroups [0, grid0) run part p0, the rest p1.
+template <int D, int RW, int KW, int KT, int ST, bool DUAL>
 __global__ void __launch_bounds__(64 * RW * KW)
     __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
-attn_bf16_kernel(const AttnParams p) {
+attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
+  const bool second = DUAL && (int)blockIdx.x >= grid0;
+  const AttnParams& p = second ? p1 : p0;
+  const int wg = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
+  const bool gated = p.decision != nullptr && p.mode != kBlock;
   constexpr int NW = RW * KW;
   constexpr int KTILE = KW * KT;                 // keys per iteration tile
   using Dma = TileDma<D, NW, KTILE>;
@@ -512,11 +518,9 @@ attn_bf16_kernel(const AttnParams p) {
   const int rw = w % RW, kg = w / RW;
   const int lr = lane & 31, hf = lane >> 5;
 
-  const Item itm = decode_item<RW * 32>(p);
+  const Item itm = decode_item<RW * 32>(p, wg);
   if (!itm.valid) return;
-  if constexpr (GATED) {
-    if (!any_recompute<RW * 32>(p, itm)) return;
-  }
+  if (gated && !any_recompute<RW * 32>(p, itm)) return;
   const bool varlen = p.cu_q != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
   const int R = G * nq;
@@ -649,7 +653,7 @@ attn_bf16_kernel(const AttnParams p) {
   }
 
   bool writer = kg == 0 && rvalid;
-  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
+  if (gated) writer = writer && p.decision[b * p.hq + h] == 0;
   const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
@@ -665,8 +669,12 @@ attn_bf16_kernel(const AttnParams p) {
 // 2u and last read (as V by group 1) in phase 2u+3, so its stage can take
 // tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
 // u+1 .. u+NS-3 may still be in flight.
-template <int D, int NS, bool GATED>
-__global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p) {
+template <int D, int NS, bool DUAL>
+__global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
+  const bool second = DUAL && (int)blockIdx.x >= grid0;
+  const AttnParams& p = second ? p1 : p0;
+  const int wg = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
+  const bool gated = p.decision != nullptr && p.mode != kBlock;
   constexpr int NW = 8, ROWS = 256, KT = 64;
   constexpr int LOOK = NS - 2;   // tiles issued ahead of the one waited for
   static_assert(LOOK >= 1 && LOOK <= 3, "ring depth");
@@ -682,11 +690,9 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p) {
   const int grp = w >> 2;
   const int lr = lane & 31, hf = lane >> 5;
 
-  const Item itm = decode_item<ROWS>(p);
+  const Item itm = decode_item<ROWS>(p, wg);
   if (!itm.valid) return;
-  if constexpr (GATED) {
-    if (!any_recompute<ROWS>(p, itm)) return;
-  }
+  if (gated && !any_recompute<ROWS>(p, itm)) return;
   const bool varlen = p.cu_q != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
   const int R = G * nq;
@@ -761,7 +767,7 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p) {
 
   const float l_tot = pair_sum(l_run);
   bool writer = rvalid;
-  if constexpr (GATED) writer = writer && p.decision[b * p.hq + h] == 0;
+  if (gated) writer = writer && p.decision[b * p.hq + h] == 0;
   const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
@@ -875,29 +881,43 @@ hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
 
 namespace {
 
-dim3 item_grid(const AttnParams& p) {
+int item_grid(const AttnParams& p) {
   const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
   const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  return dim3(per_xcd * kXcds);
+  return per_xcd * kXcds;
 }
 
+// p1 == nullptr: one part.  With two parts, p1's workgroups come first in
+// the grid (dispatch order): the caller passes the in-block part as p1, so
+// its real work starts at once while the prefix part's workgroups of reused
+// heads exit.
 template <int D, int RW, int KW, int KT, int ST>
-hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
-  const dim3 grid = item_grid(p);
-  if (p.decision != nullptr && p.mode != kBlock)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), grid, dim3(64 * RW * KW), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), grid, dim3(64 * RW * KW), 0, s, p);
+hipError_t launch_variant(const AttnParams& p0, const AttnParams* p1, hipStream_t s) {
+  const int g0 = item_grid(p0);
+  if (!p1) {
+    if (g0 == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), dim3(g0), dim3(64 * RW * KW), 0, s, p0, p0,
+                       g0);
+    return hipGetLastError();
+  }
+  const int g1 = item_grid(*p1);
+  if (g0 + g1 == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), dim3(g0 + g1), dim3(64 * RW * KW), 0, s, *p1,
+                     p0, g1);
   return hipGetLastError();
 }
 
 template <int D, int NS>
-hipError_t launch_pp(const AttnParams& p, hipStream_t s) {
-  const dim3 grid = item_grid(p);
-  if (p.decision != nullptr && p.mode != kBlock)
-    hipLaunchKernelGGL((attn_pp_kernel<D, NS, true>), grid, dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_pp_kernel<D, NS, false>), grid, dim3(512), 0, s, p);
+hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, hipStream_t s) {
+  const int g0 = item_grid(p0);
+  if (!p1) {
+    if (g0 == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_pp_kernel<D, NS, false>), dim3(g0), dim3(512), 0, s, p0, p0, g0);
+    return hipGetLastError();
+  }
+  const int g1 = item_grid(*p1);
+  if (g0 + g1 == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_pp_kernel<D, NS, true>), dim3(g0 + g1), dim3(512), 0, s, *p1, p0, g1);
   return hipGetLastError();
 }
 
@@ -927,22 +947,24 @@ int max_splits_bf16(int d, int variant) {
   return 256;
 }
 
-hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, int d, hipStream_t s) {
+hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, const AttnParams* p1, int d,
+                            hipStream_t s) {
   Bf16Plan plan = plan_in;
-  if (plan.variant == 2 && p.mode != kBlock) plan.variant = 1;  // single-wave shape: in-block only
+  // 32-key single-wave ring: in-block attention only
+  if (plan.variant == 2 && (p.mode != kBlock || (p1 && p1->mode != kBlock))) plan.variant = 1;
   if (d == 128) {
     switch (plan.variant) {
-      case 0: return launch_variant<128, 4, 1, 64, 2>(p, s);
-      case 1: return launch_variant<128, 2, 2, 32, 2>(p, s);
-      case 3: return launch_pp<128, 4>(p, s);
-      default: return launch_variant<128, 1, 1, 32, 2>(p, s);
+      case 0: return launch_variant<128, 4, 1, 64, 2>(p, p1, s);
+      case 1: return launch_variant<128, 2, 2, 32, 2>(p, p1, s);
+      case 3: return launch_pp<128, 4>(p, p1, s);
+      default: return launch_variant<128, 1, 1, 32, 2>(p, p1, s);
     }
   }
   switch (plan.variant) {
-    case 0: return launch_variant<64, 4, 1, 64, 2>(p, s);
-    case 1: return launch_variant<64, 2, 2, 32, 2>(p, s);
-    case 3: return launch_pp<64, 4>(p, s);
-    default: return launch_variant<64, 1, 1, 32, 2>(p, s);
+    case 0: return launch_variant<64, 4, 1, 64, 2>(p, p1, s);
+    case 1: return launch_variant<64, 2, 2, 32, 2>(p, p1, s);
+    case 3: return launch_pp<64, 4>(p, p1, s);
+    default: return launch_variant<64, 1, 1, 32, 2>(p, p1, s);
   }
 }
 

@@ -185,7 +185,8 @@ namespace {
 // in-block part (a_in != NULL).
 ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
                       const float* l_in, float* a_full, float* l_full, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      size_t workspace_bytes, hipStream_t stream, ba::AttnParams* block = nullptr,
+                      const ba_attn_desc* block_desc = nullptr) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
@@ -209,6 +210,14 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   p.row_tiles = pp.row_tiles;
   p.a = a_out;
   p.l = l_out;
+  if (block && desc->dtype != BA_F32) {
+    // the in-block part rides on the same launch, in the prefix plan's shape
+    // (the float32 kernel has no row tiles: one wave per row and head)
+    const int brows = sh.group * block_desc->max_q;
+    block->row_tiles = (brows + pp.bf.rows_per_wg - 1) / pp.bf.rows_per_wg;
+    if ((int64_t)block->row_tiles * block_desc->n_seq * block_desc->hkv > 0x7fffff00LL)
+      return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
+  }
   hipError_t err;
   if (desc->dtype == BA_F32 || pp.n_splits == 1) {
     p.mode = ba::kPrefixFinal;
@@ -219,7 +228,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
   }
   err = desc->dtype == BA_F32 ? ba::launch_attn_f32(p, desc->d, stream)
-                              : ba::launch_attn_bf16(pp.bf, p, desc->d, stream);
+                              : ba::launch_attn_bf16(pp.bf, p, block, desc->d, stream);
+  if (err == hipSuccess && block && desc->dtype == BA_F32) err = ba::launch_attn_f32(*block, desc->d, stream);
   if (err != hipSuccess) return hip_status(err, "prefix attention");
   if (p.mode != ba::kPrefixPartial && !merge) return BA_OK;
   // One pass combines the split partials across many workgroups (the
@@ -251,6 +261,32 @@ ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_
   return prefix_impl(desc, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream);
 }
 
+ba_status ba_split_attn(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
+                        float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  AttnShape sp, sb;
+  ba_status st = check_desc(prefix, &sp);
+  if (st != BA_OK) return st;
+  st = check_desc(block, &sb);
+  if (st != BA_OK) return st;
+  if (prefix->dtype != block->dtype || prefix->n_seq != block->n_seq || prefix->hq != block->hq ||
+      prefix->hkv != block->hkv || prefix->d != block->d || prefix->max_q != block->max_q ||
+      sp.scale != sb.scale || sp.varlen != sb.varlen || prefix->q != block->q || prefix->cu_q != block->cu_q)
+    return fail(BA_ERR_SHAPE, "prefix and block descriptors must share dtype, shapes, scale, q and cu_q");
+  if (!a_in || !l_in || !a_full) return fail(BA_ERR_NULL, "a_in, l_in and a_full are required");
+  if (prefix->n_seq == 0 || prefix->max_q == 0) return BA_OK;
+  ba::AttnParams pb = base_params(block, sb);
+  pb.decision = nullptr;
+  pb.mode = ba::kBlock;
+  pb.chunk = block->max_k > 0 ? block->max_k : 1;
+  pb.n_splits = 1;
+  pb.a = a_in;
+  pb.l = l_in;
+  return prefix_impl(prefix, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &pb,
+                     block);
+}
+
 ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache, float* a_in,
                         float* l_in, float* a_full, float* l_full, hipStream_t stream) {
   g_err.clear();
@@ -279,7 +315,7 @@ ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const fl
   p.row_tiles = (rows + bf.rows_per_wg - 1) / bf.rows_per_wg;
   if ((int64_t)p.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
     return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
-  return hip_status(ba::launch_attn_bf16(bf, p, desc->d, stream), "block attention");
+  return hip_status(ba::launch_attn_bf16(bf, p, nullptr, desc->d, stream), "block attention");
 }
 
 ba_status ba_lse_merge(int64_t rows, int32_t d, const float* a1, const float* l1, const float* a2,

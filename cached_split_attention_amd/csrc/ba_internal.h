@@ -54,7 +54,10 @@ struct Bf16Plan {
 
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix);
 int max_splits_bf16(int d, int variant);
-hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, int d, hipStream_t s);
+// One launch; with p1 non-NULL it also runs the independent part p1 (same
+// variant; its row tiles counted for plan.rows_per_wg).
+hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, const AttnParams* p1, int d,
+                            hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
 // After a prefix launch: combines split partials (p.mode == kPrefixPartial)
 // into p.a/p.l and, if p.a_full is set, merges A_out/L_out with A_in/L_in

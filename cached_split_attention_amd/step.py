@@ -4,22 +4,20 @@ FlashBlock (gist.science/es/paper/2602.05305), section 2: each step runs the
 reuse gate, recomputes the out-of-block part (A_out, L_out) only for the
 (sequence, head) pairs the gate sends to recompute (the kernel itself skips
 the others, reading the decision from device memory, so there is no
-device-to-host synchronisation), and merges it with the in-block part.  The
-in-block part (A_in, L_in) depends on neither the gate nor the cache, so it
-runs first; the prefix call then merges A_out/L_out (fresh or cached) with
-it in its last pass, so a step is three launches on one stream (a second
-stream would let the in-block part overlap the gate, but a cross-stream
-dependency inside a replayed graph costs far more than the overlap saves).
-The cache stays valid until the next block starts.  This module only orders
-calls and owns buffers; it computes nothing itself.
+device-to-host synchronisation), computes the in-block part (A_in, L_in),
+and merges the two.  The in-block part depends on neither the gate nor the
+cache, so it shares one launch with the gated prefix part, and the pass that
+combines the prefix's key splits also does the merge: a step is three
+launches on one stream.  The cache stays valid until the next block starts.
+This module only orders calls and owns buffers; it computes nothing itself.
 """
 
 from __future__ import annotations
 
 import torch
 
-from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_block_attn, ba_prefix_attn_merge,
-                  ba_prefix_attn_workspace, ba_reuse_gate, ba_reuse_gate_workspace)
+from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_prefix_attn_workspace, ba_reuse_gate,
+                  ba_reuse_gate_workspace, ba_split_attn)
 
 
 class CachedBlockAttention:
@@ -80,7 +78,6 @@ class CachedBlockAttention:
         prefix pass on the launch stream."""
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
         main = stream if stream is not None else torch.cuda.current_stream()
-        ba_block_attn(q, k, v, a_in=self.a_in, l_in=self.l_in, scale=self.scale, stream=main)
         if self.mode == BA_GATE_COUNT:
             ba_reuse_gate(self.mode, q, q_prev, k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev,
                           tau=self.tau, cache_valid=self.cache_valid, m_count=self.m_count,
@@ -90,10 +87,10 @@ class CachedBlockAttention:
                           cos=self.cos, decision=self.decision, workspace=self._gws, stream=main)
         if prefix_events is not None:
             prefix_events[0].record(main)
-        ba_prefix_attn_merge(q, self.kp, self.vp, self.a_out, self.l_out, self.a_in, self.l_in,
-                             self.a_full, self.l_full, self._ws, kv_layout=self.kv_layout,
-                             decision=self.decision if self.cache_valid else None, scale=self.scale,
-                             stream=main)
+        ba_split_attn(q, self.kp, self.vp, k, v, self.a_out, self.l_out, self.a_in, self.l_in,
+                      self.a_full, self.l_full, self._ws, kv_layout=self.kv_layout,
+                      decision=self.decision if self.cache_valid else None, scale=self.scale,
+                      stream=main)
         if prefix_events is not None:
             prefix_events[1].record(main)
         self.cache_valid = True

@@ -130,6 +130,24 @@ ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The whole split attention of one denoising step, FlashBlock "Mecanismo
+ * Central": the out-of-block part (desc `prefix`, gated by prefix->decision
+ * exactly as in ba_prefix_attn) and the in-block part (desc `block`, as
+ * ba_block_attn with a_in/l_in outputs) run in one launch, since neither
+ * depends on the other; then one pass combines the prefix's key splits and
+ * merges: A_full, L_full = merge(A_out, L_out, A_in, L_in), A_out/L_out
+ * fresh or, for reused heads, the cached ones.  Equivalent to ba_block_attn
+ * (a_in, l_in) followed by ba_prefix_attn_merge, in two launches instead of
+ * three.  The two descriptors must share dtype, n_seq, hq, hkv, d, max_q,
+ * scale, q and cu_q (they differ in k/v, their strides, cu_k and max_k).
+ * a_in, l_in, a_full are required, l_full may be NULL; the workspace is the
+ * one ba_prefix_attn_workspace(prefix) sizes.
+ */
+ba_status ba_split_attn(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
+                        float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
  * In-block attention with the fused log-space merge, FlashBlock "Mecanismo
  * Central": every query row attends over all of its sequence's block keys
  * with no mask (the block is bidirectional), giving A_in / L_in.  If a_cache

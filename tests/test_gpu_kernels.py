@@ -354,6 +354,100 @@ def test_prefix_attn_merge(dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 6, 2, 128, 900, 33), (1, 4, 4, 128, 64, 32), (3, 8, 2, 128, 700, 70),
+                                   (2, 6, 3, 64, 555, 41), (2, 4, 2, 128, 0, 20), (1, 2, 2, 128, 400, 100)])
+def test_split_attn(dtype, shape):
+    # Prefix and in-block parts in one launch, then combine and merge: the
+    # in-block result, fresh A_out of recomputed heads (cached ones left
+    # alone) and A_full against the oracle; both parts' shapes (few rows, 128
+    # and 256-row tiles, d=64, empty prefix) and a gate decision.
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=81)
+    rows = B * nb
+    if lp > 0:
+        want_a, want_l = _oracle_prefix(s)
+    else:
+        want_a, want_l = np.zeros((rows, hq, d)), np.full((rows, hq), -np.inf)
+    want_ai, want_li = _oracle_block(s)
+    r = np.random.default_rng(12)
+    cache_a = r.standard_normal((rows, hq, d)).astype(np.float32)
+    cache_l = r.standard_normal((rows, hq)).astype(np.float32)
+    dec = (r.random((B, hq)) < 0.5).astype(np.uint8)
+    dec[0, 0] = 0
+    exp_a, exp_l = want_a.copy(), want_l.copy()
+    for b in range(B):
+        for h in range(hq):
+            if dec[b, h]:
+                exp_a[b * nb:(b + 1) * nb, h] = cache_a[b * nb:(b + 1) * nb, h]
+                exp_l[b * nb:(b + 1) * nb, h] = cache_l[b * nb:(b + 1) * nb, h]
+    want_f, want_lf = oracle.merge(exp_a, exp_l, want_ai, want_li)
+    q, k, v = dev_in(s.q[0], dtype), dev_in(s.k[0], dtype), dev_in(s.v[0], dtype)
+    if lp > 0:
+        kp, vp = dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    else:
+        kp = vp = torch.zeros(B, hkv, 0, d, device=DEV, dtype=q.dtype)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    a_out = torch.from_numpy(cache_a).to(DEV)
+    l_out = torch.from_numpy(cache_l).to(DEV)
+    a_in = torch.full((rows, hq, d), 3.0, device=DEV)
+    l_in = torch.full((rows, hq), 3.0, device=DEV)
+    a_full = torch.full((rows, hq, d), 5.0, device=DEV)
+    l_full = torch.full((rows, hq), 5.0, device=DEV)
+    ba.ba_split_attn(q, kp, vp, k, v, a_out, l_out, a_in, l_in, a_full, l_full, ws,
+                     decision=torch.from_numpy(dec).to(DEV))
+    torch.cuda.synchronize()
+    check_a(host(a_in), want_ai, "A_in")
+    check_l(host(l_in), want_li, "L_in")
+    ga, gl = host(a_out), host(l_out)
+    for b in range(B):
+        for h in range(hq):
+            sl = slice(b * nb, (b + 1) * nb)
+            if dec[b, h]:
+                assert np.array_equal(ga[sl, h], cache_a[sl, h]) and np.array_equal(gl[sl, h], cache_l[sl, h])
+            else:
+                check_a(ga[sl, h], want_a[sl, h], f"A_out b{b} h{h}")
+                check_l(gl[sl, h], want_l[sl, h], f"L_out b{b} h{h}")
+    check_a(host(a_full), want_f, "A_full")
+    check_l(host(l_full), want_lf, "L_full")
+
+
+def test_split_attn_varlen():
+    # Branches of different block sizes and prefix lengths (one prefix
+    # empty), locked positions packed out, in one varlen split-attention call.
+    vb = make_varlen_batch(block_sizes=(3, 16, 40, 7), prefix_lens=(100, 0, 700, 333), h=4, d=128,
+                           lock_p=0.3, seed=21)
+    ref = oracle.run_varlen(vb)
+    n = int(vb.block_sizes.sum())
+    nbr = vb.block_sizes.size
+    cu_q = torch.empty(nbr + 1, device=DEV, dtype=torch.int32)
+    gather = torch.empty(n, device=DEV, dtype=torch.int32)
+    total = torch.empty(1, device=DEV, dtype=torch.int32)
+    qp = torch.zeros(n, vb.h, vb.d, device=DEV, dtype=torch.bfloat16)
+    ba.ba_varlen_pack(vb.block_sizes, torch.from_numpy(vb.locked).to(DEV), cu_q, gather, total, dev_bits(vb.q), qp)
+    cu_kp = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.prefix_lens)]).astype(np.int32)).to(DEV)
+    cu_kb = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.block_sizes)]).astype(np.int32)).to(DEV)
+    kp, vp = dev_bits(vb.kp), dev_bits(vb.vp)
+    kb, vbk = dev_bits(vb.k), dev_bits(vb.v)
+    max_q = int(vb.block_sizes.max())
+    outs = {nm: torch.full((n, vb.h, vb.d), 7.0, device=DEV) for nm in ("a_out", "a_in", "a_full")}
+    outs.update({nm: torch.full((n, vb.h), 7.0, device=DEV) for nm in ("l_out", "l_in", "l_full")})
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(qp, kp, vp, q_layout="thd", kv_layout="htd", cu_q=cu_q,
+                                                        cu_k=cu_kp, max_q=max_q, max_k=int(vb.prefix_lens.max()))),
+                     device=DEV, dtype=torch.uint8)
+    ba.ba_split_attn(qp, kp, vp, kb, vbk, outs["a_out"], outs["l_out"], outs["a_in"], outs["l_in"],
+                     outs["a_full"], outs["l_full"], ws, q_layout="thd", kv_layout="htd", block_kv_layout="thd",
+                     cu_q=cu_q, cu_kp=cu_kp, cu_k=cu_kb, max_q=max_q, max_kp=int(vb.prefix_lens.max()),
+                     max_k=int(vb.block_sizes.max()))
+    torch.cuda.synchronize()
+    tot = ref["total"]
+    assert int(total.item()) == tot
+    for nm in ("a_out", "a_in", "a_full"):
+        check_a(host(outs[nm])[:tot], ref[nm], nm)
+    for nm in ("l_out", "l_in", "l_full"):
+        check_l(host(outs[nm])[:tot], ref[nm], nm)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("nb", [20, 150])
 def test_prefix_attn_empty_prefix(dtype, nb):
     # nb = 150: 300 rows per KV head, the 256-row kernel

@@ -169,3 +169,18 @@ def test_workload_varlen_branches():
         check_a(ga[:, h], ref["a_full"][:, h], f"[c5_varlen] A_full head {h}")
         check_l(gl[:, h], ref["l_full"][:, h], f"[c5_varlen] L_full head {h}")
     say(f"[c5_varlen] {tot} packed rows checked on heads {heads}")
+    # the same step through the one-launch split attention (prefix and
+    # in-block parts together, then combine and merge)
+    outs = {nm: torch.empty(n, vb.h, vb.d, device=dev) for nm in ("a_out", "a_in", "a_full")}
+    outs.update({nm: torch.empty(n, vb.h, device=dev) for nm in ("l_out", "l_in", "l_full")})
+    ba.ba_split_attn(qp, kp, vp, kb, vbk, outs["a_out"], outs["l_out"], outs["a_in"], outs["l_in"],
+                     outs["a_full"], outs["l_full"], ws, q_layout="thd", kv_layout="htd", block_kv_layout="thd",
+                     cu_q=cu_q, cu_kp=cu_kp, cu_k=cu_kb, max_q=max_q, max_kp=int(vb.prefix_lens.max()),
+                     max_k=int(vb.block_sizes.max()))
+    torch.cuda.synchronize()
+    for h in heads:
+        for nm in ("a_out", "a_in", "a_full"):
+            check_a(host(outs[nm])[:tot, h], ref[nm][:, h], f"[c5_varlen split] {nm} head {h}")
+        for nm in ("l_out", "l_in", "l_full"):
+            check_l(host(outs[nm])[:tot, h], ref[nm][:, h], f"[c5_varlen split] {nm} head {h}")
+    say(f"[c5_varlen] split attention checked on heads {heads}")
