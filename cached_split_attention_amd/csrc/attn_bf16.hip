@@ -131,6 +131,14 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait for every vector-memory load of this wave, through the compiler's own
+// s_waitcnt (vmcnt 0, other counters untouched), so the compiler knows the
+// Q operand loads issued before it are complete.  Without it the compiler
+// cannot prove that inside the tile loop, and makes the first score MFMA of
+// every tile wait for vmcnt(0), which also waits out every K/V tile the
+// ring has in flight.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // As wait_barrier, also draining this wave's LDS reads first, with nothing
 // scheduled across it: a phase boundary of the alternating kernel.
 template <int N>
@@ -281,6 +289,54 @@ __device__ __forceinline__ void pv_mfma(f32x16 (&o)[D / 32], const u32x4 (&pk)[M
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
       }
     }
+}
+
+// A matrix phase of the alternating kernel: O^T += V^T P^T for the previous
+// tile (MB blocks), then S^T = K Q^T for the next, as one stream of 2*MB*DB
+// + MB*KS MFMAs whose LDS operand reads run PF MFMAs ahead of their use
+// (a rotating set of PF fragments), so the read latency hides behind the
+// MFMAs already issued instead of stalling each one.
+template <int D, int MB, int PF>
+__device__ __forceinline__ void matrix_phase(f32x16 (&o)[D / 32], const u32x4 (&pk)[MB][2], const unsigned char* sV,
+                                             f32x16 (&s)[MB], const unsigned char* sK, const OperandOffsets<D>& off,
+                                             const bf16x8 (&qf)[D / 16]) {
+  constexpr int DB = D / 32, KS = D / 16;
+  constexpr int NPV = MB * 2 * DB;    // P.V MFMAs: (block, 16-key half, 32-dim block)
+  constexpr int NS_ = KS * MB;        // score MFMAs: (k-step, block)
+  constexpr int N = NPV + NS_;
+  bf16x8 frag[PF];
+  auto read = [&](int i) -> bf16x8 {
+    if (i < NPV) {
+      const int mb = i / (2 * DB), h2 = (i / DB) % 2, db = i % DB;
+      const int kofs = (mb * 32 + 16 * h2) * (2 * D);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(sV + off.vro[db][0] + kofs));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(sV + off.vro[db][1] + kofs));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const int j = i - NPV, ks = j / MB, mb = j % MB;
+    return *reinterpret_cast<const bf16x8*>(sK + off.kro[ks] + mb * 32 * (2 * D));
+  };
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < PF; ++i) frag[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    // each step (next read, this MFMA) stays in place: the scheduler would
+    // otherwise sink the reads next to their MFMAs and expose their latency
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 a = frag[i % PF];
+    if (i + PF < N) frag[i % PF] = read(i + PF);
+    if (i < NPV) {
+      const int mb = i / (2 * DB), h2 = (i / DB) % 2, db = i % DB;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[mb][h2]), o[db], 0, 0, 0);
+    } else {
+      const int j = i - NPV, ks = j / MB, mb = j % MB;
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+    }
+  }
 }
 
 // Online softmax of one tile's scores (MB blocks starting at key g0; keys at
@@ -589,6 +645,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < n_iter) issue_tile(kb + s * KTILE, s);
+  wait_vmem_all();
 
   // The loop is unrolled over the ring so each copy reads a fixed stage.
   for (int it0 = 0; it0 < n_iter; it0 += ST) {
@@ -670,7 +727,8 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 // tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
 // u+1 .. u+NS-3 may still be in flight.
 template <int D, int NS, bool DUAL>
-__global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
   const bool second = DUAL && (int)blockIdx.x >= grid0;
   const AttnParams& p = second ? p1 : p0;
   const int wg = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
@@ -751,6 +809,7 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p0, const
 #pragma unroll
   for (int t = 0; t < LOOK; ++t)
     if (t < n) issue_tile(t);
+  wait_vmem_all();
   if (grp) even_barrier(0);
   if (grp) phase_barrier<63>(); else even_barrier(0);
   if (active && n > 0) score_mfma<D, MB>(s, smem, off, qf);
@@ -758,10 +817,11 @@ __global__ void __launch_bounds__(512) attn_pp_kernel(const AttnParams p0, const
     if (grp) even_barrier(u + 1); else phase_barrier<63>();
     if (active) softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, kb + u * KT, ke, hf);
     if (grp) phase_barrier<63>(); else even_barrier(u + 1);
-    if (active) {
-      pv_mfma<D, MB>(o, pk, smem + (u % NS) * STAGE_B + TILE_B, off);
-      if (u + 1 < n) score_mfma<D, MB>(s, smem + ((u + 1) % NS) * STAGE_B, off, qf);
-    }
+    // (after the last tile the scores are computed from a stale stage and
+    // never used: one branch-free block keeps the accumulators in place)
+    if (active)
+      matrix_phase<D, MB, 4>(o, pk, smem + (u % NS) * STAGE_B + TILE_B, s, smem + ((u + 1) % NS) * STAGE_B, off,
+                             qf);
   }
   if (!grp) phase_barrier<63>();
 
