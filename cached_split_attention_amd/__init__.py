@@ -10,6 +10,8 @@ from .api import (  # noqa: F401
     BA_GATE_COUNT,
     BA_GATE_COSINE,
     ba_block_attn,
+    ba_gated_split_attn,
+    ba_gated_split_attn_gate_workspace,
     ba_lse_merge,
     ba_prefix_attn,
     ba_prefix_attn_merge,

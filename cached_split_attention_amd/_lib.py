@@ -72,6 +72,13 @@ EXPORTS = {
     "ba_reuse_gate": (ctypes.c_int, [ctypes.POINTER(GateDesc), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]),
+    "ba_gated_split_attn_gate_workspace": (ctypes.c_size_t, [ctypes.POINTER(GateDesc)]),
+    "ba_gated_split_attn": (ctypes.c_int, [ctypes.POINTER(GateDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnDesc),
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
     "ba_varlen_pack": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

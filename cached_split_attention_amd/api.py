@@ -257,6 +257,47 @@ def ba_reuse_gate(mode, q_cur, q_prev, *, decision, workspace, k_cur=None, k_pre
                               nbytes, _stream(stream)))
 
 
+def ba_gated_split_attn_gate_workspace(mode, q_cur, q_prev, **kw) -> int:
+    g = _gate_desc(mode, q_cur, q_prev, kw.get("k_cur"), kw.get("k_prev"), kw.get("v_cur"),
+                   kw.get("v_prev"), kw.get("upd_mask"), kw.get("tau", 0), kw.get("gamma", 0.0), True)
+    return int(lib().ba_gated_split_attn_gate_workspace(ctypes.byref(g)))
+
+
+def ba_gated_split_attn(mode, q_prev, kp, vp, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None,
+                        workspace=None, *, q, decision, gate_workspace, k_prev=None, v_prev=None,
+                        upd_mask=None, tau=0, gamma=0.0, cache_valid=True, m_count=None, cos=None,
+                        kv_layout="bhsd", scale=None, stream=None):
+    """The reuse gate (q/k/v against q_prev/k_prev/v_prev; count or cosine mode) and the
+    split attention it gates, as ba_reuse_gate followed by ba_split_attn with
+    decision = (decision if cache_valid else None), in two launches.  Dense
+    block tensors [B, Nb, H, d]; `gate_workspace` is sized by
+    ba_gated_split_attn_gate_workspace and zero-filled before its first use."""
+    count = mode == BA_GATE_COUNT
+    g = _gate_desc(mode, q, q_prev, k if count else None, k_prev if count else None,
+                   v if count else None, v_prev if count else None, upd_mask, tau, gamma, cache_valid)
+    _need_gpu(decision, gate_workspace, m_count, cos)
+    _check_out(decision, (g.n_seq, g.hq), torch.uint8, "decision")
+    _check_out(m_count, (g.n_seq,), torch.int32, "m_count")
+    _check_out(cos, (g.n_seq, g.hq), torch.float64, "cos")
+    dp, rows = _desc(q, kp, vp, q_layout="bshd", kv_layout=kv_layout, cu_q=None, cu_k=None,
+                     max_q=None, max_k=None, scale=scale, decision=None)
+    db, _ = _desc(q, k, v, q_layout="bshd", kv_layout="bshd", cu_q=None, cu_k=None,
+                  max_q=None, max_k=None, scale=scale, decision=None)
+    for t, nm in ((a_out, "a_out"), (a_in, "a_in"), (a_full, "a_full")):
+        _check_out(t, (rows, dp.hq, dp.d), torch.float32, nm)
+    for t, nm in ((l_out, "l_out"), (l_in, "l_in")):
+        _check_out(t, (rows, dp.hq), torch.float32, nm)
+    if l_full is not None:
+        _check_out(l_full, (rows, dp.hq), torch.float32, "l_full")
+    _need_gpu(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    gbytes = gate_workspace.numel() * gate_workspace.element_size()
+    check(lib().ba_gated_split_attn(ctypes.byref(g), _ptr(m_count), _ptr(cos), _ptr(decision),
+                                    _ptr(gate_workspace), gbytes, ctypes.byref(dp), ctypes.byref(db),
+                                    _ptr(a_out), _ptr(l_out), _ptr(a_in), _ptr(l_in), _ptr(a_full),
+                                    _ptr(l_full), _ptr(workspace), nbytes, _stream(stream)))
+
+
 def ba_varlen_pack(block_sizes, locked, cu_seqlens_q, gather_idx, total, q_src=None, q_packed=None,
                    stream=None):
     """Pack unlocked positions (branch-major, ascending); q_src [N, h, d] rows are

@@ -50,6 +50,7 @@
 #include <math.h>
 
 #include "ba_internal.h"
+#include "gate_body.h"
 
 namespace ba {
 namespace {
@@ -532,6 +533,12 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   return it;
 }
 
+// Reuse decision of (sequence b, query head h).  Read with agent-scope loads:
+// the gate may have written it from another XCD earlier in the same launch.
+__device__ __forceinline__ bool reused(const AttnParams& p, int b, int h) {
+  return gate::ld_agent(p.decision + b * p.hq + h) != 0;
+}
+
 // True if some query head of rows [row0, row0+ROWS) needs its prefix
 // attention recomputed.
 template <int ROWS>
@@ -539,20 +546,44 @@ __device__ __forceinline__ bool any_recompute(const AttnParams& p, const Item& i
   const int R = p.group * it.nq;
   const int rlast = min(R, it.row0 + ROWS) - 1;
   bool any = false;
-  for (int g = it.row0 / it.nq; g <= rlast / it.nq; ++g) any |= p.decision[it.b * p.hq + it.kvh * p.group + g] == 0;
+  for (int g = it.row0 / it.nq; g <= rlast / it.nq; ++g) any |= !reused(p, it.b, it.kvh * p.group + g);
   return any;
+}
+
+// A gated prefix workgroup of a launch that also runs the gate: wait until
+// the gate has published sequence b's result.  One thread polls and the
+// answer is shared through LDS, so every wave takes the same path.
+// Returns 0: all heads of the workgroup are reused (nothing to do); 1: all
+// recompute (count mode with M_b >= tau, or a wait that gave up, counted in
+// ready[n_seq]); 2: the per-head decisions are written (cosine mode).
+__device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
+  __shared__ int s_r;
+  if (threadIdx.x == 0) {
+    const bool count = p.gate_mode == BA_GATE_COUNT;
+    const int r = gate::wait_ready(p.ready, b, count ? gate::kCountReady : p.hq, p.spin_limit);
+    int res;
+    if (r < 0) {
+      atomicAdd(p.ready + p.n_seq, 1);
+      res = 1;
+    } else if (count) {
+      res = (r & (gate::kCountReady - 1)) < p.gate_tau ? 0 : 1;
+    } else {
+      res = 2;
+    }
+    s_r = res;
+  }
+  __syncthreads();
+  return s_r;
 }
 
 // A launch may carry two independent parts (the prefix and the in-block
 // attention of one step): workgroups [0, grid0) run part p0, the rest p1.
-template <int D, int RW, int KW, int KT, int ST, bool DUAL>
+// With GATE, the reuse gate gp runs first, in workgroups [0, grid_g), and
+// the rest are numbered from there.
+template <int D, int RW, int KW, int KT, int ST, bool DUAL, bool GATE>
 __global__ void __launch_bounds__(64 * RW * KW)
     __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
-attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
-  const bool second = DUAL && (int)blockIdx.x >= grid0;
-  const AttnParams& p = second ? p1 : p0;
-  const int wg = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
-  const bool gated = p.decision != nullptr && p.mode != kBlock;
+attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
   constexpr int NW = RW * KW;
   constexpr int KTILE = KW * KT;                 // keys per iteration tile
   using Dma = TileDma<D, NW, KTILE>;
@@ -569,6 +600,19 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
+  int bid = (int)blockIdx.x;
+  if constexpr (GATE) {
+    if (bid < grid_g) {
+      gate::run(gp, bid, smem);
+      return;
+    }
+    bid -= grid_g;
+  }
+  const bool second = DUAL && bid >= grid0;
+  const AttnParams& p = second ? p1 : p0;
+  const int wg = second ? bid - grid0 : bid;
+  bool gated = p.decision != nullptr && p.mode != kBlock;
+
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rw = w % RW, kg = w / RW;
@@ -576,6 +620,13 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 
   const Item itm = decode_item<RW * 32>(p, wg);
   if (!itm.valid) return;
+  if constexpr (GATE) {
+    if (gated && p.ready) {
+      const int r = gate_ready(p, itm.b);
+      if (r == 0) return;
+      gated = r == 2;
+    }
+  }
   if (gated && !any_recompute<RW * 32>(p, itm)) return;
   const bool varlen = p.cu_q != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
@@ -710,7 +761,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
   }
 
   bool writer = kg == 0 && rvalid;
-  if (gated) writer = writer && p.decision[b * p.hq + h] == 0;
+  if (gated) writer = writer && !reused(p, b, h);
   const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
@@ -726,13 +777,9 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 // 2u and last read (as V by group 1) in phase 2u+3, so its stage can take
 // tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
 // u+1 .. u+NS-3 may still be in flight.
-template <int D, int NS, bool DUAL>
+template <int D, int NS, bool DUAL, bool GATE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
-  const bool second = DUAL && (int)blockIdx.x >= grid0;
-  const AttnParams& p = second ? p1 : p0;
-  const int wg = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
-  const bool gated = p.decision != nullptr && p.mode != kBlock;
+attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
   constexpr int NW = 8, ROWS = 256, KT = 64;
   constexpr int LOOK = NS - 2;   // tiles issued ahead of the one waited for
   static_assert(LOOK >= 1 && LOOK <= 3, "ring depth");
@@ -743,6 +790,19 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE_B];
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
+  int bid = (int)blockIdx.x;
+  if constexpr (GATE) {
+    if (bid < grid_g) {
+      gate::run(gp, bid, smem);
+      return;
+    }
+    bid -= grid_g;
+  }
+  const bool second = DUAL && bid >= grid0;
+  const AttnParams& p = second ? p1 : p0;
+  const int wg = second ? bid - grid0 : bid;
+  bool gated = p.decision != nullptr && p.mode != kBlock;
+
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int grp = w >> 2;
@@ -750,6 +810,13 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 
   const Item itm = decode_item<ROWS>(p, wg);
   if (!itm.valid) return;
+  if constexpr (GATE) {
+    if (gated && p.ready) {
+      const int r = gate_ready(p, itm.b);
+      if (r == 0) return;
+      gated = r == 2;
+    }
+  }
   if (gated && !any_recompute<ROWS>(p, itm)) return;
   const bool varlen = p.cu_q != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
@@ -827,7 +894,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0) {
 
   const float l_tot = pair_sum(l_run);
   bool writer = rvalid;
-  if (gated) writer = writer && p.decision[b * p.hq + h] == 0;
+  if (gated) writer = writer && !reused(p, b, h);
   const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
@@ -849,6 +916,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   constexpr int TPE = D / 4;
   constexpr int EPB = 256 / TPE;
   const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  if (p.ready && blockIdx.x == 0)
+    for (int b = threadIdx.x; b < p.n_seq; b += blockDim.x) p.ready[b] = 0;
   const int64_t e = (int64_t)blockIdx.x * EPB + threadIdx.x / TPE;
   const int t = threadIdx.x % TPE;
   if (e >= n_entries) return;
@@ -864,6 +933,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   }
   if (i >= nq) return;
   const int64_t oo = (p.cu_q ? (int64_t)(qbase + i) : vrow) * p.hq + h;
+  // With a decision to read, the loads that do not depend on it (the in-block
+  // part and, speculatively, the cached A_out/L_out) go out with it, so a
+  // reused entry costs one memory round trip.
+  float li = 0.0f, l_c = 0.0f;
+  f32x4 ai = {0.0f, 0.0f, 0.0f, 0.0f}, a_c = ai;
+  const bool spec = p.decision && p.a_full;
+  if (p.a_full) {
+    li = p.l_cache[oo];
+    ai = *reinterpret_cast<const f32x4*>(p.a_cache + oo * D + 4 * t);
+  }
+  if (spec) {
+    l_c = p.l[oo];
+    a_c = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
+  }
   // An empty prefix is written by the attention kernel's split 0.
   const bool fresh = p.mode == kPrefixPartial && nk > 0 && !(p.decision && p.decision[b * p.hq + h]);
   if (!fresh && !p.a_full) return;
@@ -903,13 +986,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     l_o = mx + __logf(den);
     *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t) = a_o;
     if (t == 0) p.l[oo] = l_o;
+  } else if (spec) {
+    a_o = a_c;
+    l_o = l_c;
   } else {
     a_o = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
     l_o = p.l[oo];
   }
   if (p.a_full) {
-    const float li = p.l_cache[oo];
-    const f32x4 ai = *reinterpret_cast<const f32x4*>(p.a_cache + oo * D + 4 * t);
     const float mm = fmaxf(l_o, li);
     f32x4 af = {0.0f, 0.0f, 0.0f, 0.0f};
     float lf = -INFINITY;
@@ -951,33 +1035,50 @@ int item_grid(const AttnParams& p) {
 // the grid (dispatch order): the caller passes the in-block part as p1, so
 // its real work starts at once while the prefix part's workgroups of reused
 // heads exit.
-template <int D, int RW, int KW, int KT, int ST>
-hipError_t launch_variant(const AttnParams& p0, const AttnParams* p1, hipStream_t s) {
+template <int D, int RW, int KW, int KT, int ST, bool CAN_GATE = true>
+hipError_t launch_variant(const AttnParams& p0, const AttnParams* p1, const GateParams* g, hipStream_t s) {
+  const GateParams none{};
   const int g0 = item_grid(p0);
   if (!p1) {
     if (g0 == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false>), dim3(g0), dim3(64 * RW * KW), 0, s, p0, p0,
-                       g0);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, false, false>), dim3(g0), dim3(64 * RW * KW), 0, s,
+                       p0, p0, g0, none, 0);
     return hipGetLastError();
   }
   const int g1 = item_grid(*p1);
+  if (g) {
+    if constexpr (CAN_GATE) {
+      const int gg = gate_grid(*g);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true, true>), dim3(gg + g0 + g1),
+                         dim3(64 * RW * KW), 0, s, *p1, p0, g1, *g, gg);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (g0 + g1 == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true>), dim3(g0 + g1), dim3(64 * RW * KW), 0, s, *p1,
-                     p0, g1);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, RW, KW, KT, ST, true, false>), dim3(g0 + g1), dim3(64 * RW * KW), 0, s,
+                     *p1, p0, g1, none, 0);
   return hipGetLastError();
 }
 
 template <int D, int NS>
-hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, hipStream_t s) {
+hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, const GateParams* g, hipStream_t s) {
+  const GateParams none{};
   const int g0 = item_grid(p0);
   if (!p1) {
     if (g0 == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_pp_kernel<D, NS, false>), dim3(g0), dim3(512), 0, s, p0, p0, g0);
+    hipLaunchKernelGGL((attn_pp_kernel<D, NS, false, false>), dim3(g0), dim3(512), 0, s, p0, p0, g0, none, 0);
     return hipGetLastError();
   }
   const int g1 = item_grid(*p1);
+  if (g) {
+    const int gg = gate_grid(*g);
+    hipLaunchKernelGGL((attn_pp_kernel<D, NS, true, true>), dim3(gg + g0 + g1), dim3(512), 0, s, *p1, p0, g1, *g,
+                       gg);
+    return hipGetLastError();
+  }
   if (g0 + g1 == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_pp_kernel<D, NS, true>), dim3(g0 + g1), dim3(512), 0, s, *p1, p0, g1);
+  hipLaunchKernelGGL((attn_pp_kernel<D, NS, true, false>), dim3(g0 + g1), dim3(512), 0, s, *p1, p0, g1, none, 0);
   return hipGetLastError();
 }
 
@@ -1008,23 +1109,24 @@ int max_splits_bf16(int d, int variant) {
 }
 
 hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, const AttnParams* p1, int d,
-                            hipStream_t s) {
+                            hipStream_t s, const GateParams* g) {
+  if (g && !p1) return hipErrorInvalidValue;
   Bf16Plan plan = plan_in;
   // 32-key single-wave ring: in-block attention only
   if (plan.variant == 2 && (p.mode != kBlock || (p1 && p1->mode != kBlock))) plan.variant = 1;
   if (d == 128) {
     switch (plan.variant) {
-      case 0: return launch_variant<128, 4, 1, 64, 2>(p, p1, s);
-      case 1: return launch_variant<128, 2, 2, 32, 2>(p, p1, s);
-      case 3: return launch_pp<128, 4>(p, p1, s);
-      default: return launch_variant<128, 1, 1, 32, 2>(p, p1, s);
+      case 0: return launch_variant<128, 4, 1, 64, 2>(p, p1, g, s);
+      case 1: return launch_variant<128, 2, 2, 32, 2>(p, p1, g, s);
+      case 3: return launch_pp<128, 4>(p, p1, g, s);
+      default: return launch_variant<128, 1, 1, 32, 2, false>(p, p1, g, s);
     }
   }
   switch (plan.variant) {
-    case 0: return launch_variant<64, 4, 1, 64, 2>(p, p1, s);
-    case 1: return launch_variant<64, 2, 2, 32, 2>(p, p1, s);
-    case 3: return launch_pp<64, 4>(p, p1, s);
-    default: return launch_variant<64, 1, 1, 32, 2>(p, p1, s);
+    case 0: return launch_variant<64, 4, 1, 64, 2>(p, p1, g, s);
+    case 1: return launch_variant<64, 2, 2, 32, 2>(p, p1, g, s);
+    case 3: return launch_pp<64, 4>(p, p1, g, s);
+    default: return launch_variant<64, 1, 1, 32, 2, false>(p, p1, g, s);
   }
 }
 

@@ -15,6 +15,11 @@ namespace {
 
 thread_local std::string g_err;
 
+// Polls (each an agent-scope load and a short sleep, about a microsecond) a
+// prefix workgroup makes for the gate of its own launch before it gives up
+// and recomputes its heads; far above the gate's running time.
+constexpr int kGateSpinLimit = 1 << 20;
+
 ba_status fail(ba_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -186,7 +191,7 @@ namespace {
 ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
                       const float* l_in, float* a_full, float* l_full, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, ba::AttnParams* block = nullptr,
-                      const ba_attn_desc* block_desc = nullptr) {
+                      const ba_attn_desc* block_desc = nullptr, const ba::GateParams* gate = nullptr) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
@@ -210,6 +215,12 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   p.row_tiles = pp.row_tiles;
   p.a = a_out;
   p.l = l_out;
+  if (gate) {
+    p.ready = gate->ready;
+    p.spin_limit = kGateSpinLimit;
+    p.gate_mode = gate->mode;
+    p.gate_tau = gate->tau;
+  }
   if (block && desc->dtype != BA_F32) {
     // the in-block part rides on the same launch, in the prefix plan's shape
     // (the float32 kernel has no row tiles: one wave per row and head)
@@ -228,7 +239,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     p.ws_l = p.ws_a + (size_t)pp.n_splits * entries * desc->d;
   }
   err = desc->dtype == BA_F32 ? ba::launch_attn_f32(p, desc->d, stream)
-                              : ba::launch_attn_bf16(pp.bf, p, block, desc->d, stream);
+                              : ba::launch_attn_bf16(pp.bf, p, block, desc->d, stream, gate);
   if (err == hipSuccess && block && desc->dtype == BA_F32) err = ba::launch_attn_f32(*block, desc->d, stream);
   if (err != hipSuccess) return hip_status(err, "prefix attention");
   if (p.mode != ba::kPrefixPartial && !merge) return BA_OK;
@@ -261,10 +272,13 @@ ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_
   return prefix_impl(desc, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream);
 }
 
-ba_status ba_split_attn(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
-                        float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
+namespace {
+
+// Prefix part and in-block part in one launch (with the gate, if given, in
+// the same launch), then the combine-and-merge pass.
+ba_status split_impl(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
+                     float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, const ba::GateParams* gate) {
   AttnShape sp, sb;
   ba_status st = check_desc(prefix, &sp);
   if (st != BA_OK) return st;
@@ -284,7 +298,17 @@ ba_status ba_split_attn(const ba_attn_desc* prefix, const ba_attn_desc* block, f
   pb.a = a_in;
   pb.l = l_in;
   return prefix_impl(prefix, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &pb,
-                     block);
+                     block, gate);
+}
+
+}  // namespace
+
+ba_status ba_split_attn(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
+                        float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  return split_impl(prefix, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream,
+                    nullptr);
 }
 
 ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const float* l_cache, float* a_in,
@@ -337,9 +361,11 @@ size_t ba_reuse_gate_workspace(const ba_gate_desc* g) {
   return ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
 }
 
-ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, uint8_t* decision, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
+namespace {
+
+// Validates a gate call and fills its launch parameters.
+ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint8_t* decision, void* workspace,
+                      size_t workspace_bytes, ba::GateParams* out) {
   if (!g) return fail(BA_ERR_NULL, "gate descriptor is NULL");
   if (g->mode != BA_GATE_COUNT && g->mode != BA_GATE_COSINE) return fail(BA_ERR_SHAPE, "unknown gate mode %d", g->mode);
   if (g->dtype != BA_BF16 && g->dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", g->dtype);
@@ -366,8 +392,8 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, ui
   const size_t need = ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
   if (!workspace || workspace_bytes < need)
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
-  if (g->n_seq == 0) return BA_OK;
-  ba::GateParams p{};
+  ba::GateParams& p = *out;
+  p = ba::GateParams{};
   p.mode = g->mode;
   p.esize = esize_of(g->dtype);
   p.n_seq = g->n_seq;
@@ -407,7 +433,66 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, ui
   p.ws_int = static_cast<int32_t*>(workspace);
   const size_t nbh = (size_t)g->n_seq * g->hq;
   p.ws_dbl = reinterpret_cast<double*>(static_cast<char*>(workspace) + ((nbh * sizeof(int32_t) + 15) & ~(size_t)15));
+  return BA_OK;
+}
+
+// Bytes of a fused call's gate workspace: the gate's own, then the
+// per-sequence ready counts and the count of waits that gave up.
+size_t fused_gate_ws_bytes(const ba_gate_desc* g) {
+  const size_t own = ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
+  return ((own + 15) & ~(size_t)15) + ((size_t)g->n_seq + 1) * sizeof(int32_t);
+}
+
+}  // namespace
+
+ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos, uint8_t* decision, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  ba::GateParams p;
+  const ba_status st = gate_params(g, m_count, cos, decision, workspace, workspace_bytes, &p);
+  if (st != BA_OK) return st;
+  if (g->n_seq == 0) return BA_OK;
   return hip_status(ba::launch_gate(p, stream), "reuse gate");
+}
+
+size_t ba_gated_split_attn_gate_workspace(const ba_gate_desc* g) {
+  if (!g || g->n_seq < 0 || g->hq < 1 || g->n_blk < 1 || g->d < 1) return 0;
+  return fused_gate_ws_bytes(g);
+}
+
+ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double* cos, uint8_t* decision,
+                              void* gate_workspace, size_t gate_workspace_bytes, const ba_attn_desc* prefix,
+                              const ba_attn_desc* block, float* a_out, float* l_out, float* a_in, float* l_in,
+                              float* a_full, float* l_full, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  g_err.clear();
+  if (!prefix || !block) return fail(BA_ERR_NULL, "attention descriptor is NULL");
+  ba::GateParams gp;
+  ba_status st = gate_params(gate, m_count, cos, decision, gate_workspace, gate_workspace_bytes, &gp);
+  if (st != BA_OK) return st;
+  if (gate_workspace_bytes < fused_gate_ws_bytes(gate))
+    return fail(BA_ERR_WORKSPACE, "gate workspace of %zu bytes needed, %zu given", fused_gate_ws_bytes(gate),
+                gate_workspace_bytes);
+  if (gate->n_seq != prefix->n_seq || gate->hq != prefix->hq || gate->n_blk != prefix->max_q ||
+      gate->dtype != prefix->dtype)
+    return fail(BA_ERR_SHAPE, "gate and attention descriptors must share n_seq, hq, block size and dtype");
+  if (prefix->decision) return fail(BA_ERR_SHAPE, "the prefix descriptor's decision must be NULL (the gate's is used)");
+  // The prefix part is gated by this call's decisions only when the cache
+  // is valid; otherwise every head recomputes and nothing waits.
+  ba_attn_desc pd = *prefix;
+  pd.decision = gate->cache_valid ? decision : nullptr;
+  if (prefix->dtype == BA_F32 || prefix->n_seq == 0 || prefix->max_q == 0) {
+    // no fused launch for the float32 kernel: the gate, then the split pass
+    if (prefix->n_seq > 0) {
+      const hipError_t e = ba::launch_gate(gp, stream);
+      if (e != hipSuccess) return hip_status(e, "reuse gate");
+    }
+    return split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream,
+                      nullptr);
+  }
+  const size_t own = ba::gate_workspace_bytes(gate->mode, gate->n_seq, gate->hq, gate->n_blk, gate->d);
+  gp.ready = reinterpret_cast<int32_t*>(static_cast<char*>(gate_workspace) + ((own + 15) & ~(size_t)15));
+  return split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &gp);
 }
 
 ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host, const uint8_t* locked,

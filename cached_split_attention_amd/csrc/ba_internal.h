@@ -41,6 +41,16 @@ struct AttnParams {
   const float* l_cache;
   float* a_full;
   float* l_full;
+  // Gate run by the same launch: a gated prefix part first waits until the
+  // gate has published sequence b's result in ready[b] (count mode: M_b,
+  // from which it decides itself against gate_tau; cosine mode: all hq
+  // decisions written), polling at most spin_limit times; a wait that gives
+  // up counts itself in ready[n_seq] and recomputes its heads.  The combine
+  // pass after such a launch zeroes ready[0 .. n_seq).
+  int32_t* ready;
+  int spin_limit;
+  int gate_mode;
+  int gate_tau;
 };
 
 
@@ -54,10 +64,6 @@ struct Bf16Plan {
 
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix);
 int max_splits_bf16(int d, int variant);
-// One launch; with p1 non-NULL it also runs the independent part p1 (same
-// variant; its row tiles counted for plan.rows_per_wg).
-hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, const AttnParams* p1, int d,
-                            hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
 // After a prefix launch: combines split partials (p.mode == kPrefixPartial)
 // into p.a/p.l and, if p.a_full is set, merges A_out/L_out with A_in/L_in
@@ -98,7 +104,16 @@ struct GateParams {
   uint8_t* decision;
   int32_t* ws_int;     // tickets / counters
   double* ws_dbl;      // cosine partials
+  int32_t* ready;      // NULL, or per-sequence counts of decisions written
 };
+int gate_grid(const GateParams& p);
+
+// One launch; with p1 non-NULL it also runs the independent part p1 (same
+// variant; its row tiles counted for plan.rows_per_wg).  With g non-NULL as
+// well, the gate runs in the first workgroups of the same launch and the
+// prefix part p waits for it per sequence (p.ready == g->ready).
+hipError_t launch_attn_bf16(const Bf16Plan& plan, const AttnParams& p, const AttnParams* p1, int d,
+                            hipStream_t s, const GateParams* g = nullptr);
 int gate_cos_chunks(int n_blk, int d);
 size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d);
 hipError_t launch_gate(const GateParams& p, hipStream_t s);

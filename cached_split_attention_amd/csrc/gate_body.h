@@ -1,0 +1,247 @@
+// Workgroup bodies of the two reuse gates of FlashBlock
+// (gist.science/es/paper/2602.05305, section 2, "Estrategias de Reutilizacion
+// Adaptativa"), shared by the stand-alone gate kernels and by the attention
+// launch that runs the gate in its first workgroups:
+//   count  - M_b = number of block positions whose Q, K or V row changed
+//            (bitwise) since the previous step; reuse iff M_b < tau;
+//   cosine - per head, the cosine of the block Q against the previous step's,
+//            accumulated in float64; reuse iff cos > gamma.
+// Workgroups publish partial results, take a ticket with an integer atomic,
+// and the last workgroup of each sequence (count) or (sequence, head)
+// (cosine) finishes the reduction in a fixed order and resets its ticket, so
+// the workspace is zero again when the launch ends.  Only integer atomics
+// are used; float64 partials are summed in chunk order, so results are
+// bitwise reproducible for a given workgroup size.  Partials and decisions
+// cross workgroups (and XCDs) through agent-scope stores and loads, never
+// through whole-cache flushes.
+//
+// With p.ready set, the gate also publishes its result to consumers in the
+// same launch through ready[b] (zero before the launch):
+//   count  - the workgroup that finishes sequence b stores kCountReady | M_b
+//            there (consumers derive the decision, the same for every head,
+//            from M_b, so they need not read the decision bytes);
+//   cosine - the workgroup that finishes (b, h) adds 1 once decision[b, h]
+//            is written, so ready[b] == hq means all of b's are there.
+#pragma once
+
+#include <math.h>
+
+#include "ba_internal.h"
+
+namespace ba {
+namespace gate {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCountReady = 1 << 30;   // count mode: ready[b] = kCountReady | M_b
+
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stores of this thread acknowledged (performed at the agent's coherence
+// point) before whatever follows.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename W>
+__device__ __forceinline__ bool words_differ(const W& x, const W& y) {
+  if constexpr (sizeof(W) == 16) {
+    return (x[0] != y[0]) | (x[1] != y[1]) | (x[2] != y[2]) | (x[3] != y[3]);
+  } else {
+    return x != y;
+  }
+}
+
+// Does any Q, K or V row of block position (b, pos) differ between cur and
+// prev?  The position's words (Q heads, then K heads, then V heads; W = the
+// comparison word) are spread over the workgroup, 16 per thread per round,
+// with all of a round's loads issued before any comparison so a round costs
+// one memory latency (one round covers 64 KB of cur and of prev at 256
+// threads and 16-byte words).
+template <typename W>
+__device__ bool position_changed(const GateParams& p, int b, int pos) {
+  const int wpr = p.d * p.esize / (int)sizeof(W);
+  const int nq = p.hq * wpr;
+  const int nk = p.k_cur ? p.hkv * wpr : 0;
+  const int nv = p.v_cur ? p.hkv * wpr : 0;
+  const int total = nq + nk + nv;
+  constexpr int U = 16;
+  bool diff = false;
+  for (int t0 = threadIdx.x; t0 < total; t0 += U * (int)blockDim.x) {
+    W x[U], y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int w = t0 + u * (int)blockDim.x;
+      x[u] = W{};
+      y[u] = W{};
+      if (w < total) {
+        const void* cur = p.q_cur;
+        const void* prev = p.q_prev;
+        int64_t s0 = p.qs0, s1 = p.qs1, s2 = p.qs2;
+        if (w >= nq) {
+          w -= nq;
+          const bool isv = w >= nk;
+          if (isv) w -= nk;
+          cur = isv ? p.v_cur : p.k_cur;
+          prev = isv ? p.v_prev : p.k_prev;
+          s0 = p.ks0;
+          s1 = p.ks1;
+          s2 = p.ks2;
+        }
+        const int hh = w / wpr, wi = w - hh * wpr;
+        const int64_t off = ((int64_t)b * s0 + (int64_t)pos * s1 + (int64_t)hh * s2) * p.esize;
+        x[u] = reinterpret_cast<const W*>(static_cast<const char*>(cur) + off)[wi];
+        y[u] = reinterpret_cast<const W*>(static_cast<const char*>(prev) + off)[wi];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) diff |= words_differ(x[u], y[u]);
+  }
+  return diff;
+}
+
+// Count gate, one workgroup per (block position pos, sequence b).  s_m: one
+// int of LDS.
+template <typename W>
+__device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
+  bool diff = false;
+  if (p.upd_mask) {
+    diff = threadIdx.x == 0 && p.upd_mask[(int64_t)b * p.n_blk + pos] != 0;
+  } else {
+    diff = position_changed<W>(p, b, pos);
+  }
+  diff = __syncthreads_or(diff);
+  // One atomic per workgroup carries both the ticket (low 16 bits) and the
+  // count of changed positions (high 16 bits); the last workgroup of the
+  // sequence reads the total from its own return value and resets the word.
+  if (threadIdx.x == 0) {
+    const unsigned old = atomicAdd(reinterpret_cast<unsigned*>(p.ws_int) + b, (diff ? 0x10000u : 0u) + 1u);
+    *s_m = -1;
+    if ((int)(old & 0xffffu) == p.n_blk - 1) {
+      const int m = (int)(old >> 16) + (diff ? 1 : 0);
+      *s_m = m;
+      if (p.ready) atomicExch(p.ready + b, kCountReady | m);
+      atomicExch(p.ws_int + b, 0);
+      p.m_count[b] = m;
+    }
+  }
+  __syncthreads();
+  const int m = *s_m;
+  if (m < 0) return;
+  const uint8_t dec = (p.cache_valid && m < p.tau) ? 1 : 0;
+  for (int h = threadIdx.x; h < p.hq; h += blockDim.x) st_agent(p.decision + (int64_t)b * p.hq + h, dec);
+}
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx, int esize) {
+  if (esize == 2) {
+    const uint16_t u = static_cast<const uint16_t*>(base)[idx];
+    return __uint_as_float((unsigned)u << 16);
+  }
+  return static_cast<const float*>(base)[idx];
+}
+
+// Cosine gate, one workgroup per (position chunk c, head h, sequence b).
+// red: 3 * blockDim.x doubles of LDS (blockDim.x a power of two).
+__device__ void cos_body(const GateParams& p, int c, int h, int b, double* red) {
+  const int nt = (int)blockDim.x, t = (int)threadIdx.x;
+  const int per = (p.n_blk + p.chunks - 1) / p.chunks;
+  const int p0 = min(p.n_blk, c * per), p1 = min(p.n_blk, p0 + per);
+  const int n = (p1 - p0) * p.d;
+  double dot = 0.0, nc = 0.0, np = 0.0;
+  for (int e = t; e < n; e += nt) {
+    const int pos = p0 + e / p.d, dd = e - (e / p.d) * p.d;
+    const int64_t idx = (int64_t)b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + dd;
+    const double x = load_elem(p.q_cur, idx, p.esize);
+    const double y = load_elem(p.q_prev, idx, p.esize);
+    dot = fma(x, y, dot);
+    nc = fma(x, x, nc);
+    np = fma(y, y, np);
+  }
+  red[t] = dot;
+  red[nt + t] = nc;
+  red[2 * nt + t] = np;
+  __syncthreads();
+  for (int s = nt / 2; s > 0; s >>= 1) {
+    if (t < s) {
+      red[t] += red[t + s];
+      red[nt + t] += red[nt + t + s];
+      red[2 * nt + t] += red[2 * nt + t + s];
+    }
+    __syncthreads();
+  }
+  if (t != 0) return;
+  const int64_t bh = (int64_t)b * p.hq + h;
+  double* part = p.ws_dbl + (bh * p.chunks + c) * 3;
+  st_agent(part + 0, red[0]);
+  st_agent(part + 1, red[nt]);
+  st_agent(part + 2, red[2 * nt]);
+  stores_done();  // partials acknowledged before the ticket
+  int32_t* ticket = p.ws_int + bh;
+  const int tk = atomicAdd(ticket, 1);
+  if (tk != p.chunks - 1) return;
+  // The XCD's L2 may hold stale lines of the partials: drop them first.
+  asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
+  double sd = 0.0, sc = 0.0, sp = 0.0;
+  for (int k = 0; k < p.chunks; ++k) {
+    double* q = p.ws_dbl + (bh * p.chunks + k) * 3;
+    sd += ld_agent(q + 0);
+    sc += ld_agent(q + 1);
+    sp += ld_agent(q + 2);
+    st_agent(q + 0, 0.0);
+    st_agent(q + 1, 0.0);
+    st_agent(q + 2, 0.0);
+  }
+  atomicExch(ticket, 0);
+  double cs = 0.0;
+  uint8_t dec = 0;
+  if (sc != 0.0 && sp != 0.0) {
+    cs = sd / (sqrt(sc) * sqrt(sp));
+    dec = (p.cache_valid && cs > p.gamma) ? 1 : 0;
+  }
+  if (p.cos) p.cos[bh] = cs;
+  st_agent(p.decision + bh, dec);
+  if (p.ready) {
+    stores_done();
+    atomicAdd(p.ready + b, 1);
+  }
+}
+
+// Gate workgroup wg of a grid of gate_grid(p) workgroups (count: position
+// fastest, then sequence; cosine: chunk, head, sequence); lds is scratch of
+// at least 3 * blockDim.x doubles.
+__device__ __forceinline__ void run(const GateParams& p, int wg, void* lds) {
+  if (p.mode == BA_GATE_COUNT) {
+    const int pos = wg % p.n_blk, b = wg / p.n_blk;
+    int* s_m = static_cast<int*>(lds);
+    if (p.vec16)
+      count_body<u32x4>(p, pos, b, s_m);
+    else if (p.esize == 4)
+      count_body<uint32_t>(p, pos, b, s_m);
+    else
+      count_body<uint16_t>(p, pos, b, s_m);
+  } else {
+    const int c = wg % p.chunks, h = (wg / p.chunks) % p.hq, b = wg / (p.chunks * p.hq);
+    cos_body(p, c, h, b, static_cast<double*>(lds));
+  }
+}
+
+// Wait until ready[b] reaches target (count mode: kCountReady; cosine: hq),
+// polling with agent-scope loads; returns the word read, or -1 after
+// `limit` polls.
+__device__ __forceinline__ int wait_ready(const int32_t* ready, int b, int target, int limit) {
+  for (int n = 0; n < limit; ++n) {
+    const int r = __builtin_amdgcn_readfirstlane(ld_agent(ready + b));
+    if (r >= target) return r;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return -1;
+}
+
+}  // namespace gate
+}  // namespace ba

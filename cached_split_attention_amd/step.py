@@ -1,23 +1,25 @@
-"""One denoising step of cached split attention, as a sequence of library calls.
+"""One denoising step of cached split attention, as library calls.
 
 FlashBlock (gist.science/es/paper/2602.05305), section 2: each step runs the
 reuse gate, recomputes the out-of-block part (A_out, L_out) only for the
 (sequence, head) pairs the gate sends to recompute (the kernel itself skips
 the others, reading the decision from device memory, so there is no
 device-to-host synchronisation), computes the in-block part (A_in, L_in),
-and merges the two.  The in-block part depends on neither the gate nor the
-cache, so it shares one launch with the gated prefix part, and the pass that
-combines the prefix's key splits also does the merge: a step is three
-launches on one stream.  The cache stays valid until the next block starts.
-This module only orders calls and owns buffers; it computes nothing itself.
+and merges the two.  One call does it all (ba_gated_split_attn): the gate,
+the in-block part and the gated prefix part share one launch (the prefix
+workgroups wait for their sequence's decisions; the in-block part needs
+none), and the pass that combines the prefix's key splits also does the
+merge, so a step is two launches on one stream.  The cache stays valid
+until the next block starts.  This module only orders calls and owns
+buffers; it computes nothing itself.
 """
 
 from __future__ import annotations
 
 import torch
 
-from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_prefix_attn_workspace, ba_reuse_gate,
-                  ba_reuse_gate_workspace, ba_split_attn)
+from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_gated_split_attn, ba_gated_split_attn_gate_workspace,
+                  ba_prefix_attn_workspace)
 
 
 class CachedBlockAttention:
@@ -66,33 +68,24 @@ class CachedBlockAttention:
             self._ws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
         if self._gws is None:
             kw = {} if self.mode == BA_GATE_COSINE else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
-            n = ba_reuse_gate_workspace(self.mode, q, q_prev, **kw)
+            n = ba_gated_split_attn_gate_workspace(self.mode, q, q_prev, **kw)
             self._gws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
 
-    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None, prefix_events=None):
+    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None):
         """Run one step; returns (a_full, l_full) views of the output buffers.
 
         With no valid cache the gate still runs (it reports M), but the prefix
-        pass is launched without the decision: everything recomputes.
-        prefix_events: optional (start, end) events recorded around the
-        prefix pass on the launch stream."""
+        part is not gated by it: everything recomputes."""
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
         main = stream if stream is not None else torch.cuda.current_stream()
-        if self.mode == BA_GATE_COUNT:
-            ba_reuse_gate(self.mode, q, q_prev, k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev,
-                          tau=self.tau, cache_valid=self.cache_valid, m_count=self.m_count,
-                          decision=self.decision, workspace=self._gws, stream=main)
-        else:
-            ba_reuse_gate(self.mode, q, q_prev, gamma=self.gamma, cache_valid=self.cache_valid,
-                          cos=self.cos, decision=self.decision, workspace=self._gws, stream=main)
-        if prefix_events is not None:
-            prefix_events[0].record(main)
-        ba_split_attn(q, self.kp, self.vp, k, v, self.a_out, self.l_out, self.a_in, self.l_in,
-                      self.a_full, self.l_full, self._ws, kv_layout=self.kv_layout,
-                      decision=self.decision if self.cache_valid else None, scale=self.scale,
-                      stream=main)
-        if prefix_events is not None:
-            prefix_events[1].record(main)
+        count = self.mode == BA_GATE_COUNT
+        ba_gated_split_attn(self.mode, q_prev, self.kp, self.vp, k, v, self.a_out, self.l_out, self.a_in,
+                            self.l_in, self.a_full, self.l_full, self._ws, q=q, decision=self.decision,
+                            gate_workspace=self._gws, k_prev=k_prev if count else None,
+                            v_prev=v_prev if count else None, tau=self.tau, gamma=self.gamma,
+                            cache_valid=self.cache_valid, m_count=self.m_count if count else None,
+                            cos=None if count else self.cos, kv_layout=self.kv_layout, scale=self.scale,
+                            stream=main)
         self.cache_valid = True
         return self.a_full, self.l_full
 
@@ -104,8 +97,8 @@ class CachedBlockAttention:
         block (no valid cache); otherwise the cache is taken as valid.
         Replaying the graph re-runs those steps on the same buffers.
         Workspaces are allocated before capture and no memset is recorded
-        (the gate's workspace is cleared by its own kernels), so replays need
-        no re-initialisation.
+        (the gate's tickets are cleared by its own workgroups and its ready
+        counts by the combine pass), so replays need no re-initialisation.
         """
         steps = list(steps)
         self.start_block(kp, vp)

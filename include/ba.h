@@ -216,6 +216,35 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos,
                         hipStream_t stream);
 
 /*
+ * One denoising step with the reuse gate in the same launch as the split
+ * attention (FlashBlock, section 2: the gate of "Estrategias de
+ * Reutilizacion Adaptativa" decides, per head, whether the out-of-block part
+ * of "Mecanismo Central" is recomputed or reused).  Equivalent to
+ * ba_reuse_gate(gate, ...) followed by ba_split_attn(prefix', block, ...),
+ * where prefix' is *prefix with decision = (gate->cache_valid ? decision :
+ * NULL), but in two launches instead of three: the gate's workgroups come
+ * first in the attention launch and each gated prefix workgroup waits (with
+ * agent-scope loads, bounded) until the gate has written its sequence's
+ * decisions; the in-block part does not wait.
+ *   gate, m_count, cos, decision: as for ba_reuse_gate; gate->n_seq, hq,
+ *     dtype and n_blk must equal prefix->n_seq, hq, dtype and max_q.
+ *   gate_workspace: ba_gated_split_attn_gate_workspace(gate) bytes, zero-
+ *     filled before first use; every call that returns BA_OK leaves it zero
+ *     again except for its last int32, which counts prefix workgroups that
+ *     gave up waiting for the gate (then they recomputed their heads, which
+ *     is exact attention; it stays 0 unless the device stalls for about a
+ *     second).  A call whose launch fails leaves it undefined: zero it again.
+ *   prefix->decision must be NULL; everything else as for ba_split_attn.
+ * The float32 dtype runs the two calls in sequence (no fused launch).
+ */
+size_t ba_gated_split_attn_gate_workspace(const ba_gate_desc* gate);
+ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double* cos, uint8_t* decision,
+                              void* gate_workspace, size_t gate_workspace_bytes,
+                              const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out,
+                              float* l_out, float* a_in, float* l_in, float* a_full, float* l_full,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Varlen packing of unlocked query positions across branches (BlockBatch
  * "Optimisation Systeme"; SURELOCK "Accion de Bloqueo").  Branch b owns block
  * positions sum(block_sizes_host[:b]) .. ; a position with locked[p] != 0

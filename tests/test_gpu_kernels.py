@@ -411,6 +411,90 @@ def test_split_attn(dtype, shape):
     check_l(host(l_full), want_lf, "L_full")
 
 
+GATED_SHAPES = [
+    # (B, hq, hkv, d, lp, nb): few rows (two key-waves, split-KV), 128-row
+    # tiles (GQA), the alternating 256-row kernel, d = 64
+    (2, 8, 8, 128, 512, 32),
+    (2, 8, 2, 128, 600, 32),
+    (2, 4, 1, 128, 700, 80),
+    (2, 4, 4, 64, 300, 20),
+]
+
+
+@pytest.mark.parametrize("mode", ["count", "cosine"])
+@pytest.mark.parametrize("shape", GATED_SHAPES)
+def test_gated_split_attn(mode, shape):
+    # The gate in the attention launch (prefix workgroups waiting for their
+    # sequence's decisions) gives what the gate followed by the split pass
+    # gives: same decisions and M, attention outputs bit for bit.  Three
+    # calls in a row (the ready counts must be reset in between): valid
+    # cache with mixed decisions, valid cache again, and no valid cache.
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=91)
+    rows = B * nb
+    q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
+    kp, vp = dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
+    r = np.random.default_rng(5)
+    if mode == "count":
+        # sequence 0: one changed position (reuse at tau = 4); sequence 1: five
+        q_prev, k_prev, v_prev = q.clone(), k.clone(), v.clone()
+        q_prev[0, 3] += 1.0
+        for pos in (0, 2, 5, 7, nb - 1):
+            (k_prev if pos % 2 else v_prev)[1, pos] += 1.0
+        gate_kw = dict(tau=4)
+        bmode = ba.BA_GATE_COUNT
+    else:
+        sig = torch.from_numpy(r.uniform(0.01, 0.8, size=(1, 1, hq, 1)).astype(np.float32)).to(DEV)
+        q_prev = (q.float() + sig * torch.randn(q.shape, device=DEV)).to(torch.bfloat16)
+        k_prev = v_prev = None
+        gate_kw = dict(gamma=0.9)
+        bmode = ba.BA_GATE_COSINE
+    cache_a = torch.from_numpy(r.standard_normal((rows, hq, d)).astype(np.float32)).to(DEV)
+    cache_l = torch.from_numpy(r.standard_normal((rows, hq)).astype(np.float32)).to(DEV)
+    nws = max(1, ba.ba_prefix_attn_workspace(q, kp, vp))
+    gkw = {} if mode == "cosine" else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
+
+    def buffers():
+        return dict(a_out=cache_a.clone(), l_out=cache_l.clone(),
+                    a_in=torch.full((rows, hq, d), 3.0, device=DEV), l_in=torch.full((rows, hq), 3.0, device=DEV),
+                    a_full=torch.full((rows, hq, d), 5.0, device=DEV), l_full=torch.full((rows, hq), 5.0, device=DEV),
+                    dec=torch.full((B, hq), 7, device=DEV, dtype=torch.uint8),
+                    m=torch.full((B,), -1, device=DEV, dtype=torch.int32),
+                    cos=torch.zeros(B, hq, device=DEV, dtype=torch.float64),
+                    ws=torch.zeros(nws, device=DEV, dtype=torch.uint8))
+
+    ref, fused = buffers(), buffers()
+    gws_ref = torch.zeros(max(1, ba.ba_reuse_gate_workspace(bmode, q, q_prev, **gkw)), device=DEV, dtype=torch.uint8)
+    gws = torch.zeros(ba.ba_gated_split_attn_gate_workspace(bmode, q, q_prev, **gkw), device=DEV, dtype=torch.uint8)
+    count = mode == "count"
+    for call, valid in enumerate((True, True, False)):
+        ba.ba_reuse_gate(bmode, q, q_prev, decision=ref["dec"], workspace=gws_ref, cache_valid=valid,
+                         m_count=ref["m"] if count else None, cos=None if count else ref["cos"], **gkw, **gate_kw)
+        ba.ba_split_attn(q, kp, vp, k, v, ref["a_out"], ref["l_out"], ref["a_in"], ref["l_in"], ref["a_full"],
+                         ref["l_full"], ref["ws"], decision=ref["dec"] if valid else None)
+        ba.ba_gated_split_attn(bmode, q_prev, kp, vp, k, v, fused["a_out"], fused["l_out"], fused["a_in"],
+                               fused["l_in"], fused["a_full"], fused["l_full"], fused["ws"], q=q,
+                               decision=fused["dec"], gate_workspace=gws, k_prev=k_prev, v_prev=v_prev,
+                               cache_valid=valid, m_count=fused["m"] if count else None,
+                               cos=None if count else fused["cos"], **gate_kw)
+        torch.cuda.synchronize()
+        assert torch.equal(fused["dec"], ref["dec"]), f"call {call}: decisions differ"
+        if count:
+            assert torch.equal(fused["m"], ref["m"])
+            if call == 0:
+                assert host(ref["dec"]).tolist() == [[1] * hq, [0] * hq], "schedule should mix reuse and recompute"
+        else:
+            # the two reductions differ in workgroup size only
+            assert np.allclose(host(fused["cos"]), host(ref["cos"]), rtol=0, atol=1e-12)
+            if call == 0:
+                dv = host(ref["dec"])
+                assert 0 < dv.sum() < dv.size, "gamma should mix reuse and recompute"
+        for nm in ("a_out", "l_out", "a_in", "l_in", "a_full", "l_full"):
+            assert torch.equal(fused[nm], ref[nm]), f"call {call}: {nm} differs"
+        gw = host(gws).view(np.int32)
+        assert not gw.any(), "gate workspace not left zero (ready counts, tickets or timeouts)"
+
+
 def test_split_attn_varlen():
     # Branches of different block sizes and prefix lengths (one prefix
     # empty), locked positions packed out, in one varlen split-attention call.
