@@ -560,7 +560,8 @@ __device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
   __shared__ int s_r;
   if (threadIdx.x == 0) {
     const bool count = p.gate_mode == BA_GATE_COUNT;
-    const int r = gate::wait_ready(p.ready, b, count ? gate::kCountReady : p.hq, p.spin_limit);
+    const int32_t* word = p.ready + (int)(blockIdx.x % kReadyCopies) * p.ready_stride + b;
+    const int r = gate::wait_ready(word, count ? gate::kCountReady : p.hq, p.spin_limit);
     int res;
     if (r < 0) {
       atomicAdd(p.ready + p.n_seq, 1);
@@ -917,7 +918,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   constexpr int EPB = 256 / TPE;
   const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
   if (p.ready && blockIdx.x == 0)
-    for (int b = threadIdx.x; b < p.n_seq; b += blockDim.x) p.ready[b] = 0;
+    for (int c = 0; c < kReadyCopies; ++c)
+      for (int b = threadIdx.x; b < p.n_seq; b += blockDim.x) p.ready[c * p.ready_stride + b] = 0;
   const int64_t e = (int64_t)blockIdx.x * EPB + threadIdx.x / TPE;
   const int t = threadIdx.x % TPE;
   if (e >= n_entries) return;

@@ -217,6 +217,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   p.l = l_out;
   if (gate) {
     p.ready = gate->ready;
+    p.ready_stride = gate->ready_stride;
     p.spin_limit = kGateSpinLimit;
     p.gate_mode = gate->mode;
     p.gate_tau = gate->tau;
@@ -436,11 +437,14 @@ ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint
   return BA_OK;
 }
 
-// Bytes of a fused call's gate workspace: the gate's own, then the
-// per-sequence ready counts and the count of waits that gave up.
+// A fused call's gate workspace: the gate's own, then kReadyCopies copies of
+// the per-sequence ready words (each copy n_seq + 1 ints rounded up to a
+// 128-byte line; int n_seq of copy 0 counts waits that gave up).
+size_t ready_stride_ints(const ba_gate_desc* g) { return ((size_t)g->n_seq + 1 + 31) & ~(size_t)31; }
+
 size_t fused_gate_ws_bytes(const ba_gate_desc* g) {
   const size_t own = ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
-  return ((own + 15) & ~(size_t)15) + ((size_t)g->n_seq + 1) * sizeof(int32_t);
+  return ((own + 127) & ~(size_t)127) + ba::kReadyCopies * ready_stride_ints(g) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -491,7 +495,8 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
                       nullptr);
   }
   const size_t own = ba::gate_workspace_bytes(gate->mode, gate->n_seq, gate->hq, gate->n_blk, gate->d);
-  gp.ready = reinterpret_cast<int32_t*>(static_cast<char*>(gate_workspace) + ((own + 15) & ~(size_t)15));
+  gp.ready = reinterpret_cast<int32_t*>(static_cast<char*>(gate_workspace) + ((own + 127) & ~(size_t)127));
+  gp.ready_stride = (int)ready_stride_ints(gate);
   return split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &gp);
 }
 

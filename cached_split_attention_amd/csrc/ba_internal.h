@@ -44,10 +44,12 @@ struct AttnParams {
   // Gate run by the same launch: a gated prefix part first waits until the
   // gate has published sequence b's result in ready[b] (count mode: M_b,
   // from which it decides itself against gate_tau; cosine mode: all hq
-  // decisions written), polling at most spin_limit times; a wait that gives
-  // up counts itself in ready[n_seq] and recomputes its heads.  The combine
-  // pass after such a launch zeroes ready[0 .. n_seq).
+  // decisions written), polling copy (workgroup % kReadyCopies) of the
+  // ready words at most spin_limit times; a wait that gives up counts itself
+  // in ready[n_seq] and recomputes its heads.  The combine pass after such a
+  // launch zeroes ready[0 .. n_seq) of every copy.
   int32_t* ready;
+  int ready_stride;
   int spin_limit;
   int gate_mode;
   int gate_tau;
@@ -104,8 +106,10 @@ struct GateParams {
   uint8_t* decision;
   int32_t* ws_int;     // tickets / counters
   double* ws_dbl;      // cosine partials
-  int32_t* ready;      // NULL, or per-sequence counts of decisions written
+  int32_t* ready;      // NULL, or the ready words (kReadyCopies copies)
+  int ready_stride;    // ints between copies
 };
+constexpr int kReadyCopies = 8;
 int gate_grid(const GateParams& p);
 
 // One launch; with p1 non-NULL it also runs the independent part p1 (same

@@ -16,12 +16,17 @@
 // through whole-cache flushes.
 //
 // With p.ready set, the gate also publishes its result to consumers in the
-// same launch through ready[b] (zero before the launch):
+// same launch through ready words (zero before the launch), kept in
+// kReadyCopies copies p.ready_stride ints apart so that the many polling
+// workgroups spread over several memory channels (a workgroup polls copy
+// blockIdx % kReadyCopies):
 //   count  - the workgroup that finishes sequence b stores kCountReady | M_b
-//            there (consumers derive the decision, the same for every head,
-//            from M_b, so they need not read the decision bytes);
-//   cosine - the workgroup that finishes (b, h) adds 1 once decision[b, h]
-//            is written, so ready[b] == hq means all of b's are there.
+//            in every copy of ready[b] (consumers derive the decision, the
+//            same for every head, from M_b, so they need not read the
+//            decision bytes);
+//   cosine - the workgroup that finishes (b, h) adds 1 to every copy once
+//            decision[b, h] is written, so ready[b] == hq means all of b's
+//            are there.
 #pragma once
 
 #include <math.h>
@@ -34,6 +39,7 @@ namespace gate {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCountReady = 1 << 30;   // count mode: ready[b] = kCountReady | M_b
+
 
 template <typename T>
 __device__ __forceinline__ T ld_agent(const T* p) {
@@ -126,7 +132,8 @@ __device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
     if ((int)(old & 0xffffu) == p.n_blk - 1) {
       const int m = (int)(old >> 16) + (diff ? 1 : 0);
       *s_m = m;
-      if (p.ready) atomicExch(p.ready + b, kCountReady | m);
+      if (p.ready)
+        for (int c = 0; c < kReadyCopies; ++c) atomicExch(p.ready + c * p.ready_stride + b, kCountReady | m);
       atomicExch(p.ws_int + b, 0);
       p.m_count[b] = m;
     }
@@ -208,7 +215,7 @@ __device__ void cos_body(const GateParams& p, int c, int h, int b, double* red) 
   st_agent(p.decision + bh, dec);
   if (p.ready) {
     stores_done();
-    atomicAdd(p.ready + b, 1);
+    for (int c = 0; c < kReadyCopies; ++c) atomicAdd(p.ready + c * p.ready_stride + b, 1);
   }
 }
 
@@ -231,12 +238,12 @@ __device__ __forceinline__ void run(const GateParams& p, int wg, void* lds) {
   }
 }
 
-// Wait until ready[b] reaches target (count mode: kCountReady; cosine: hq),
-// polling with agent-scope loads; returns the word read, or -1 after
-// `limit` polls.
-__device__ __forceinline__ int wait_ready(const int32_t* ready, int b, int target, int limit) {
+// Wait until the ready word at `word` reaches target (count mode:
+// kCountReady; cosine: hq), polling with agent-scope loads; returns the word
+// read, or -1 after `limit` polls.
+__device__ __forceinline__ int wait_ready(const int32_t* word, int target, int limit) {
   for (int n = 0; n < limit; ++n) {
-    const int r = __builtin_amdgcn_readfirstlane(ld_agent(ready + b));
+    const int r = __builtin_amdgcn_readfirstlane(ld_agent(word));
     if (r >= target) return r;
     __builtin_amdgcn_s_sleep(2);
   }

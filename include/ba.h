@@ -230,10 +230,10 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos,
  *     dtype and n_blk must equal prefix->n_seq, hq, dtype and max_q.
  *   gate_workspace: ba_gated_split_attn_gate_workspace(gate) bytes, zero-
  *     filled before first use; every call that returns BA_OK leaves it zero
- *     again except for its last int32, which counts prefix workgroups that
- *     gave up waiting for the gate (then they recomputed their heads, which
- *     is exact attention; it stays 0 unless the device stalls for about a
- *     second).  A call whose launch fails leaves it undefined: zero it again.
+ *     again, except that prefix workgroups that gave up waiting for the gate
+ *     (after about a second; they then recompute their heads, which is exact
+ *     attention) are counted in one of its int32 words.  A call whose launch
+ *     fails leaves it undefined: zero it again.
  *   prefix->decision must be NULL; everything else as for ba_split_attn.
  * The float32 dtype runs the two calls in sequence (no fused launch).
  */
