@@ -109,7 +109,7 @@ struct GateParams {
   int32_t* ready;      // NULL, or the ready words (kReadyCopies copies)
   int ready_stride;    // ints between copies
 };
-constexpr int kReadyCopies = 8;
+constexpr int kReadyCopies = 4;
 int gate_grid(const GateParams& p);
 
 // One launch; with p1 non-NULL it also runs the independent part p1 (same
