@@ -14,7 +14,9 @@ totalling at least 1 GiB so a recompute reads it from HBM, not from the
 
 Prints one JSON line.  value = algorithmic bytes moved per second (GB/s);
 TFLOP/s, per-step latencies, the prefix kernel's roofline and the CPU
-oracle's rate on a bounded sample ride along.
+oracle's rate on a bounded sample ride along.  --workload selects another of
+the workload shapes; the multi-branch varlen one (c5_varlen) times one step
+with a cold cache (varlen packing, then the split attention).
 """
 
 from __future__ import annotations
@@ -61,6 +63,27 @@ def step_work(s, dec, esize=2):
                  + 2 * B * nb * hq * (d + 1) * 4)
     blk_flops = 4 * d * nb * nb * B * hq
     return p_bytes + gate_bytes + blk_bytes, p_flops + blk_flops, p_bytes, p_flops
+
+
+def varlen_work(vb, total):
+    """Algorithmic (bytes, flops, prefix_bytes, prefix_flops) of one step of
+    the multi-branch varlen batch vb with a cold cache and `total` unlocked
+    (packed) query rows: the lock mask read and the packing indices written,
+    the unlocked Q rows gathered (read and written), every branch's prefix
+    K/V, the packed Q read by the attention, A_out/L_out written and read by
+    the merge, the block K/V, A_full/L_full written."""
+    import numpy as np
+    H, d, es = vb.h, vb.d, 2
+    bs = vb.block_sizes.astype(np.int64)
+    ltot, btot, nbr = int(vb.prefix_lens.sum()), int(bs.sum()), int(bs.size)
+    pack = btot + (nbr + 1) * 4 + btot * 4 + 4 + 2 * total * H * d * es
+    p_bytes = 2 * ltot * H * d * es + total * H * d * es + total * H * (d + 1) * 4
+    blk_bytes = 2 * btot * H * d * es + total * H * (d + 1) * 4 + total * H * (d + 1) * 4
+    starts = np.concatenate([[0], np.cumsum(bs)])
+    u = np.array([int((vb.locked[starts[b]:starts[b + 1]] == 0).sum()) for b in range(nbr)], dtype=np.int64)
+    p_flops = int(4 * d * H * (u * vb.prefix_lens.astype(np.int64)).sum())
+    blk_flops = int(4 * d * H * (u * bs).sum())
+    return pack + p_bytes + blk_bytes, p_flops + blk_flops, p_bytes, p_flops
 
 
 # ----------------------------------------------------------------------------
@@ -154,6 +177,171 @@ def probe(args, s, q, kps, vps):
     print(json.dumps({"probe": args.workload, "prefix_passes": 2 * len(kps),
                       "copy_bytes_each": COPY_PROBE_BYTES, "copies": 4}), flush=True)
 
+def roofline_of(p_bytes, p_flops, us):
+    """The roof a pass of this arithmetic intensity reaches first, and the
+    fraction of it achieved in `us` microseconds."""
+    achieved = p_bytes / (us * 1e-6) / 1e9
+    achieved_tf = p_flops / (us * 1e-6) / 1e12
+    if p_flops / p_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    return roof, achieved, achieved_tf
+
+
+def run_varlen(args):
+    """The multi-branch varlen workload: one step with a cold cache = the
+    packing of unlocked positions, then the split attention (prefix and
+    in-block parts in one launch, then combine and merge), captured as one
+    HIP graph per rotated prefix copy."""
+    import numpy as np
+    import torch
+    import cached_split_attention_amd as ba
+    from workloads import preset
+
+    dev = torch.device("cuda:0")
+    vb = preset(args.workload)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    n = int(vb.block_sizes.sum())
+    nbr = int(vb.block_sizes.size)
+    kp0, vp0 = to_dev(vb.kp), to_dev(vb.vp)
+    kv_bytes = 2 * kp0.numel() * 2
+    n_copies = max(1, int(math.ceil(args.cold_bytes * (1 << 30) / kv_bytes)))
+    kps = [kp0] + [kp0.clone() for _ in range(n_copies - 1)]
+    vps = [vp0] + [vp0.clone() for _ in range(n_copies - 1)]
+    q_all, kb, vbk = to_dev(vb.q), to_dev(vb.k), to_dev(vb.v)
+    locked = torch.from_numpy(vb.locked).to(dev)
+    cu_q = torch.empty(nbr + 1, device=dev, dtype=torch.int32)
+    gather = torch.empty(n, device=dev, dtype=torch.int32)
+    total = torch.empty(1, device=dev, dtype=torch.int32)
+    qp = torch.zeros(n, vb.h, vb.d, device=dev, dtype=torch.bfloat16)
+    cu_kp = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.prefix_lens)]).astype(np.int32)).to(dev)
+    cu_kb = torch.from_numpy(np.concatenate([[0], np.cumsum(vb.block_sizes)]).astype(np.int32)).to(dev)
+    max_q, max_kp, max_kb = int(vb.block_sizes.max()), int(vb.prefix_lens.max()), int(vb.block_sizes.max())
+    outs = {nm: torch.empty(n, vb.h, vb.d, device=dev) for nm in ("a_out", "a_in", "a_full")}
+    outs.update({nm: torch.empty(n, vb.h, device=dev) for nm in ("l_out", "l_in", "l_full")})
+    pkw = dict(q_layout="thd", kv_layout="htd", cu_q=cu_q, cu_k=cu_kp, max_q=max_q, max_k=max_kp,
+               scale=vb.scale)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(qp, kp0, vp0, **pkw)), device=dev, dtype=torch.uint8)
+
+    def step(i, stream=None):
+        ba.ba_varlen_pack(vb.block_sizes, locked, cu_q, gather, total, q_all, qp, stream=stream)
+        ba.ba_split_attn(qp, kps[i], vps[i], kb, vbk, outs["a_out"], outs["l_out"], outs["a_in"], outs["l_in"],
+                         outs["a_full"], outs["l_full"], ws, q_layout="thd", kv_layout="htd",
+                         block_kv_layout="thd", cu_q=cu_q, cu_kp=cu_kp, cu_k=cu_kb, max_q=max_q,
+                         max_kp=max_kp, max_k=max_kb, scale=vb.scale, stream=stream)
+
+    def prefix_pass(i, stream=None):
+        ba.ba_prefix_attn(qp, kps[i], vps[i], outs["a_out"], outs["l_out"], ws, stream=stream, **pkw)
+
+    step(0)
+    torch.cuda.synchronize()
+    n_total = int(total.item())
+    if args.probe:
+        for i in range(2 * n_copies):
+            prefix_pass(i % n_copies)
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_PROBE_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": args.workload, "prefix_passes": 2 * n_copies,
+                          "copy_bytes_each": COPY_PROBE_BYTES, "copies": 4}), flush=True)
+        return
+    stream = torch.cuda.current_stream()
+
+    def capture(fn, i):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                fn(i, stream=torch.cuda.current_stream())
+        stream.wait_stream(side)
+        return g
+
+    graphs = [capture(step, i) for i in range(n_copies)]
+    pgraphs = [capture(prefix_pass, i) for i in range(n_copies)]
+
+    def timed(fn, n_rep):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n_rep):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_rep
+
+    for i in range(args.warmup):
+        graphs[i % n_copies].replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    w0 = time.perf_counter()
+    ms_per_step = timed(lambda i: graphs[(args.warmup + i) % n_copies].replay(), K)
+    wall = time.perf_counter() - w0
+    pref_us = timed(lambda i: pgraphs[i % n_copies].replay(), max(4, 2 * n_copies)) * 1e3
+
+    s_bytes, s_flops, p_bytes, p_flops = varlen_work(vb, n_total)
+    roof, achieved, achieved_tf = roofline_of(p_bytes, p_flops, pref_us)
+    out = {
+        "metric": METRIC,
+        "value": round(s_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic, seeded (workloads.preset), resident in HBM",
+        "config": {"workload": f"{args.workload}: branches with block sizes {vb.block_sizes.tolist()}, "
+                               f"prefixes {vb.prefix_lens.tolist()}, H={vb.h} d={vb.d}, "
+                               f"{n_total} unlocked of {n} positions",
+                   "bench_step": "one step with a cold cache (varlen pack, then split attention), "
+                                 "replayed as a HIP graph",
+                   "prefix_kv_copies": n_copies},
+        "tflops": round(s_flops / (ms_per_step * 1e-3) / 1e12, 4),
+        "latency_us": {"step": round(ms_per_step * 1e3, 2), "prefix_pass": round(pref_us, 2)},
+        "roofline": {
+            "kernel": "prefix pass (varlen, every branch): split-KV attention kernel + split combine kernel, "
+                      "back to back",
+            **roof,
+            "traffic": measured_traffic(args.workload),
+            "algorithmic_bytes_per_launch": p_bytes,
+            "algorithmic_flops_per_launch": p_flops,
+            "gbs": round(achieved, 1),
+            "tflops": round(achieved_tf, 3),
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            threads = 1
+        heads = list(range(0, vb.h, 4))
+        t0 = time.perf_counter()
+        oracle.run_varlen(vb, heads=heads)
+        dt = time.perf_counter() - t0
+        frac = len(heads) / vb.h
+        out["cpu_baseline"] = {"value": s_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"one step of the same batch on {len(heads)} of {vb.h} heads "
+                                         f"(bytes scaled to those heads), NumPy float64, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +358,11 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    f"--gpus {args.gpus} is not supported"}), flush=True)
         sys.exit(2)
+
+    from workloads.synth import VARLEN_PRESETS
+    if args.workload in VARLEN_PRESETS:
+        run_varlen(args)
+        return
 
     import numpy as np
     import torch
@@ -257,17 +450,8 @@ def main():
     n_roof = 4
     pref_mean_us = timed(lambda i: pgraph.replay(), n_roof) * 1e3 / n_copies
     p_bytes1, p_flops1 = work[0][2], work[0][3]
-    achieved = p_bytes1 / (pref_mean_us * 1e-6) / 1e9
-    achieved_tf = p_flops1 / (pref_mean_us * 1e-6) / 1e12
     traffic = measured_traffic(args.workload)
-    # the pass is bound by whichever roof its arithmetic intensity reaches first
-    mfma_bound = p_flops1 / p_bytes1 > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof, achieved, achieved_tf = roofline_of(p_bytes1, p_flops1, pref_mean_us)
 
     out = {
         "metric": METRIC,
