@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     BA_GATE_COUNT,
     BA_GATE_COSINE,
     ba_block_attn,
+    ba_debug_set_gate_spin_limit,
     ba_gated_split_attn,
     ba_gated_split_attn_gate_workspace,
     ba_lse_merge,

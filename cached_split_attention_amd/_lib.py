@@ -84,6 +84,7 @@ EXPORTS = {
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "ba_debug_set_gate_spin_limit": (ctypes.c_int32, [ctypes.c_int32]),
     "ba_last_error": (ctypes.c_char_p, []),
     "ba_version": (ctypes.c_int32, []),
 }

@@ -16,9 +16,10 @@ import torch
 from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_COSINE,
                    c_i64x2, check, lib)
 
-__all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_block_attn", "ba_lse_merge",
-           "ba_reuse_gate_workspace", "ba_reuse_gate", "ba_varlen_pack", "ba_version",
-           "BA_GATE_COUNT", "BA_GATE_COSINE"]
+__all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge", "ba_split_attn",
+           "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
+           "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
+           "ba_debug_set_gate_spin_limit", "BA_GATE_COUNT", "BA_GATE_COSINE"]
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -114,6 +115,12 @@ def _check_out(t, shape, dtype, name):
 
 def ba_version() -> int:
     return lib().ba_version()
+
+
+def ba_debug_set_gate_spin_limit(polls: int) -> int:
+    """Testing aid: polls a gated prefix workgroup of ba_gated_split_attn makes for its
+    gate before giving up (negative = default); returns the previous value."""
+    return int(lib().ba_debug_set_gate_spin_limit(int(polls)))
 
 
 def ba_prefix_attn_workspace(q, k, v, *, q_layout="bshd", kv_layout="bhsd", cu_q=None, cu_k=None,

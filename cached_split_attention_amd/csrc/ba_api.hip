@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "ba_internal.h"
@@ -17,8 +18,10 @@ thread_local std::string g_err;
 
 // Polls (each an agent-scope load and a short sleep, about a microsecond) a
 // prefix workgroup makes for the gate of its own launch before it gives up
-// and recomputes its heads; far above the gate's running time.
+// and recomputes its heads; far above the gate's running time.  Tests lower
+// it through ba_debug_set_gate_spin_limit to exercise the give-up path.
 constexpr int kGateSpinLimit = 1 << 20;
+std::atomic<int> g_spin_limit{kGateSpinLimit};
 
 ba_status fail(ba_status st, const char* fmt, ...) {
   char buf[512];
@@ -178,6 +181,12 @@ const char* ba_last_error(void) { return g_err.c_str(); }
 
 int32_t ba_version(void) { return (1 << 16) | 0; }
 
+int32_t ba_debug_set_gate_spin_limit(int32_t polls) {
+  const int prev = g_spin_limit.load();
+  g_spin_limit.store(polls < 0 ? kGateSpinLimit : polls);
+  return prev;
+}
+
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
@@ -218,7 +227,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   if (gate) {
     p.ready = gate->ready;
     p.ready_stride = gate->ready_stride;
-    p.spin_limit = kGateSpinLimit;
+    p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     p.gate_mode = gate->mode;
     p.gate_tau = gate->tau;
   }

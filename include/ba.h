@@ -265,6 +265,16 @@ ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host,
                          const void* q_src, const int64_t q_src_stride[2], void* q_packed,
                          hipStream_t stream);
 
+/*
+ * Testing aid for the callers' failure-handling tests, not for production
+ * use: sets how many times a prefix workgroup of ba_gated_split_attn polls
+ * for its gate before giving up (negative restores the default, about a
+ * second); returns the previous value.  Applies to calls made after it, from
+ * any thread.  With 0, every gated prefix workgroup gives up at once,
+ * recomputes its heads and is counted in the gate workspace.
+ */
+int32_t ba_debug_set_gate_spin_limit(int32_t polls);
+
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* ba_last_error(void);
 

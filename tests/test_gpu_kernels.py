@@ -495,6 +495,77 @@ def test_gated_split_attn(mode, shape):
         assert not gw.any(), "gate workspace not left zero (ready counts, tickets or timeouts)"
 
 
+@pytest.mark.parametrize("mode", ["count", "cosine"])
+def test_gated_split_attn_gives_up(mode):
+    # The prefix workgroups' bounded wait for the gate, forced to give up at
+    # once from the host (spin limit 0): every gated prefix workgroup counts
+    # itself in the gate workspace and recomputes its heads.  With split
+    # partials the combine pass still applies the gate's decisions, so the
+    # outputs equal those of the gate followed by the split pass.
+    B, hq, hkv, d, lp, nb = 2, 8, 8, 128, 512, 32
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=93)
+    rows = B * nb
+    q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
+    kp, vp = dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
+    nws = ba.ba_prefix_attn_workspace(q, kp, vp)
+    assert nws > 0, "shape must use split partials"
+    if mode == "count":
+        q_prev, k_prev, v_prev = q.clone(), k.clone(), v.clone()
+        for pos in range(6):
+            q_prev[1, pos] += 1.0        # sequence 0 reused, sequence 1 recomputed
+        bmode, gkw, gate_kw = ba.BA_GATE_COUNT, dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev), dict(tau=4)
+    else:
+        q_prev = (q.float() + 0.3 * torch.randn(q.shape, device=DEV, generator=torch.Generator(DEV).manual_seed(3))
+                  ).to(torch.bfloat16)
+        k_prev = v_prev = None
+        q_prev[0] = q[0]                 # sequence 0 reused (cosine 1)
+        bmode, gkw, gate_kw = ba.BA_GATE_COSINE, {}, dict(gamma=0.99)
+    r = np.random.default_rng(7)
+    cache_a = torch.from_numpy(r.standard_normal((rows, hq, d)).astype(np.float32)).to(DEV)
+    cache_l = torch.from_numpy(r.standard_normal((rows, hq)).astype(np.float32)).to(DEV)
+    outs = {}
+    for which in ("ref", "fused"):
+        o = dict(a_out=cache_a.clone(), l_out=cache_l.clone(), a_in=torch.empty(rows, hq, d, device=DEV),
+                 l_in=torch.empty(rows, hq, device=DEV), a_full=torch.empty(rows, hq, d, device=DEV),
+                 l_full=torch.empty(rows, hq, device=DEV), dec=torch.empty(B, hq, device=DEV, dtype=torch.uint8),
+                 m=torch.empty(B, device=DEV, dtype=torch.int32), cos=torch.empty(B, hq, device=DEV, dtype=torch.float64),
+                 ws=torch.zeros(nws, device=DEV, dtype=torch.uint8))
+        count = mode == "count"
+        if which == "ref":
+            gws = torch.zeros(max(1, ba.ba_reuse_gate_workspace(bmode, q, q_prev, **gkw)), device=DEV, dtype=torch.uint8)
+            ba.ba_reuse_gate(bmode, q, q_prev, decision=o["dec"], workspace=gws, m_count=o["m"] if count else None,
+                             cos=None if count else o["cos"], **gkw, **gate_kw)
+            ba.ba_split_attn(q, kp, vp, k, v, o["a_out"], o["l_out"], o["a_in"], o["l_in"], o["a_full"], o["l_full"],
+                             o["ws"], decision=o["dec"])
+        else:
+            gws = torch.zeros(ba.ba_gated_split_attn_gate_workspace(bmode, q, q_prev, **gkw), device=DEV,
+                              dtype=torch.uint8)
+            prev = ba.ba_debug_set_gate_spin_limit(0)
+            try:
+                ba.ba_gated_split_attn(bmode, q_prev, kp, vp, k, v, o["a_out"], o["l_out"], o["a_in"], o["l_in"],
+                                       o["a_full"], o["l_full"], o["ws"], q=q, decision=o["dec"], gate_workspace=gws,
+                                       k_prev=k_prev, v_prev=v_prev, m_count=o["m"] if count else None,
+                                       cos=None if count else o["cos"], **gate_kw)
+                torch.cuda.synchronize()
+            finally:
+                ba.ba_debug_set_gate_spin_limit(prev)
+            o["gws"] = gws
+        torch.cuda.synchronize()
+        outs[which] = o
+    ref, fused = outs["ref"], outs["fused"]
+    dv = host(ref["dec"])
+    assert dv[0].all() and not dv[1].any(), "schedule should reuse sequence 0 and recompute sequence 1"
+    assert torch.equal(fused["dec"], ref["dec"])
+    gave_up = int(host(fused["gws"]).view(np.int32).sum())
+    assert gave_up > 0, "no prefix workgroup was counted as giving up"
+    for nm in ("a_in", "l_in", "a_full", "l_full"):
+        assert torch.allclose(fused[nm], ref[nm], rtol=1e-6, atol=1e-6), nm
+    # recomputed heads' A_out is fresh either way; reused heads keep the cache
+    for nm in ("a_out", "l_out"):
+        assert torch.equal(fused[nm][nb:], ref[nm][nb:]), nm
+        assert torch.equal(fused[nm][:nb], ref[nm][:nb]), nm
+
+
 def test_split_attn_varlen():
     # Branches of different block sizes and prefix lengths (one prefix
     # empty), locked positions packed out, in one varlen split-attention call.
