@@ -350,6 +350,8 @@ def main():
     ap.add_argument("--workload", default="c2_llada")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated prefix copies")
+    ap.add_argument("--lp", type=int, default=None,
+                    help="prefix length override for the dense shapes (long-context sweep)")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: only the prefix pass, eagerly, over the rotated copies, "
                          "then a plain device copy of known size (the counters' scale reference)")
@@ -370,7 +372,12 @@ def main():
     from workloads import preset
 
     dev = torch.device("cuda:0")
-    s = preset(args.workload)
+
+    def progress(msg):
+        print(f"[bench {args.workload}] {msg}", file=sys.stderr, flush=True)
+
+    s = preset(args.workload) if args.lp is None else preset(args.workload, lp=args.lp)
+    progress(f"inputs drawn (prefix {s.lp})")
 
     def to_dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -402,6 +409,7 @@ def main():
     rec_steps = [t for t in range(1, s.steps + 1) if (decisions[t] == 0).any()]
     reuse_steps = [t for t in range(2, s.steps + 1) if t not in rec_steps]
 
+    progress(f"eager pass done, {len(rec_steps)} recompute steps")
     # one graph per prefix copy: the whole block schedule
     graphs = [attn.capture_block(q, k, v, kps[i], vps[i]) for i in range(n_copies)]
     # single-step graphs for per-step latency
@@ -427,6 +435,7 @@ def main():
     ms_per_step = timed(lambda i: graphs[(args.warmup + 1 + i) % n_copies].replay(), K)
     wall = time.perf_counter() - w0
 
+    progress("block schedules timed")
     rec_us = timed(lambda i: g_rec.replay(), 20) * 1e3
     reuse_us = timed(lambda i: g_reuse.replay(), 50) * 1e3 if g_reuse is not None else None
 

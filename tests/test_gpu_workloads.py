@@ -52,8 +52,8 @@ def _sampled_rows(sched, t, gates_hist, last, rows, got_a, got_l):
         check_l(got_l[r, h][None], lf, f"L_full step {t} (b{b} h{h} i{i})")
 
 
-def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=False, seed=0):
-    sched = preset(name)
+def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=False, seed=0, **overrides):
+    sched = preset(name, **overrides)
     say(f"[{name}] B={sched.B} Hq={sched.hq} Hkv={sched.hkv} d={sched.d} Lp={sched.lp} Nb={sched.nb} "
         f"steps={sched.steps} gate={sched.gate}")
     gates = oracle.step_gates(sched)
@@ -122,6 +122,13 @@ def test_workload_gqa_long_context():
 def test_workload_video():
     sched, rec = _run_schedule_checked("c4_video", rows_per_step=6, use_graph=False, seed=4)
     assert sched.B * sched.hq < rec < sched.steps * sched.B * sched.hq  # some heads reuse
+
+
+def test_workload_long_prefix():
+    # The pages' long-context axis: the LLaDA-like heads over a 256k-token
+    # prefix, four steps (many key splits per head, and their combine).
+    sched, rec = _run_schedule_checked("c2_llada", rows_per_step=3, seed=6, lp=262144, steps=4)
+    assert rec >= sched.B * sched.hq
 
 
 def test_workload_varlen_branches():
