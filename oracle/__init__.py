@@ -14,6 +14,8 @@ from .reference import (  # noqa: F401
     step_gates,
     refresh_steps,
     prefix_rows,
+    block_keys,
+    prefix_rows_in_blocks,
     block_rows,
     run_block,
     run_varlen,

@@ -20,6 +20,9 @@ Sources (gist.science summaries):
   [BB]  "Resume Technique : BlockBatch" (fr/paper/2605.29233), "Methodologie",
         "Optimisation Systeme": unmasked query positions of all branches are
         packed into one variable-length buffer.
+  [FB] also, in "Estrategias de Reutilizacion Adaptativa", sparse attention:
+        the keys a sparse pass leaves out are the "out" set whose contribution
+        is cached and merged with the fresh pass over the selected keys.
 
 Readings of points the pages leave open (each is listed in the design notes):
   softmax scale s given by the caller (1/sqrt(d) by default); L is a natural
@@ -266,6 +269,29 @@ def prefix_rows(sched, t_ref: int, b: int, h: int, rows=None):
         q = q[rows]
     k = to_f64(sched.kp[b, h // g], sched.dtype)
     v = to_f64(sched.vp[b, h // g], sched.dtype)
+    return attention(q, k, v, sched.scale)
+
+
+def block_keys(blocks, lp: int, block_keys: int = 64) -> np.ndarray:
+    """Key indices of a list of key blocks: block j is keys
+    [block_keys*j, block_keys*(j+1)) clipped to the prefix length."""
+    idx = [np.arange(block_keys * j, min(block_keys * (j + 1), lp)) for j in np.asarray(blocks, dtype=np.int64)]
+    return np.concatenate(idx) if idx else np.zeros(0, dtype=np.int64)
+
+
+def prefix_rows_in_blocks(sched, t_ref: int, b: int, h: int, blocks, rows=None):
+    """(A, L) of query head h of sequence b over the prefix keys of the listed
+    blocks only.  [FB] Estrategias de Reutilizacion Adaptativa, sparse
+    attention: a sparse pass attends over the selected keys, and the
+    unselected keys are the "out" set whose contribution is cached; both are
+    plain attention over a key subset, joined by the Mecanismo Central merge."""
+    g = sched.hq // sched.hkv
+    q = to_f64(sched.q[t_ref][b, :, h, :], sched.dtype)
+    if rows is not None:
+        q = q[rows]
+    sel = block_keys(blocks, sched.lp)
+    k = to_f64(sched.kp[b, h // g][sel], sched.dtype)
+    v = to_f64(sched.vp[b, h // g][sel], sched.dtype)
     return attention(q, k, v, sched.scale)
 
 

@@ -176,3 +176,39 @@ def test_generator_is_seeded_and_shaped():
     assert a.kp.shape == (2, 2, 40, 16) and a.q[0].shape == (2, 12, 4, 16)
     assert a.k[3].shape == (2, 12, 2, 16) and a.kp.dtype == np.uint16
     assert math.isclose(a.scale, 0.25)
+
+
+def test_key_blocks_cover_the_prefix_once():
+    # a selected list and its complement cover every prefix key exactly once,
+    # the last (ragged) block clipped to the prefix length
+    from workloads import make_key_block_lists
+    lp = 64 * 9 + 17
+    sel, rest = make_key_block_lists(B=2, hkv=3, lp=lp, density=0.4, seed=5)
+    assert sel.shape == (2, 3, 4) and rest.shape == (2, 3, 6)
+    for b in range(2):
+        for g in range(3):
+            keys = np.concatenate([oracle.block_keys(sel[b, g], lp), oracle.block_keys(rest[b, g], lp)])
+            assert np.array_equal(np.sort(keys), np.arange(lp))
+    assert oracle.block_keys([9], lp).tolist() == list(range(576, lp))
+    assert oracle.block_keys([], lp).size == 0
+
+
+def test_sparse_residual_split_is_exact():
+    # [FB] sparse attention with the unselected keys as the cached "out" set:
+    # merging the selected-block pass with the complementary (residual) pass
+    # is attention over the whole prefix (to rounding); an empty selection
+    # weighs nothing
+    from workloads import make_key_block_lists
+    s = make_block_schedule(dtype="bf16", B=1, hq=4, hkv=2, d=32, lp=64 * 7 + 5, nb=6, steps=0, std=1.0,
+                            schedule="none", seed=12)
+    sel, rest = make_key_block_lists(B=1, hkv=2, lp=s.lp, density=0.3, seed=2)
+    for h in range(4):
+        a1, l1 = oracle.prefix_rows_in_blocks(s, 0, 0, h, sel[0, h // 2])
+        a2, l2 = oracle.prefix_rows_in_blocks(s, 0, 0, h, rest[0, h // 2])
+        am, lm = oracle.merge(a1, l1, a2, l2)
+        af, lf = oracle.prefix_rows(s, 0, 0, h)
+        assert np.max(np.abs(am - af)) < 1e-12 and np.max(np.abs(lm - lf)) < 1e-12
+        a0, l0 = oracle.prefix_rows_in_blocks(s, 0, 0, h, [])
+        assert np.all(a0 == 0) and np.all(np.isneginf(l0))
+        ae, le = oracle.merge(a0, l0, af, lf)
+        assert np.max(np.abs(ae - af)) < 1e-15 and np.max(np.abs(le - lf)) < 1e-15

@@ -11,6 +11,7 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     round_to_bf16_bits,
     make_block_schedule,
+    make_key_block_lists,
     make_varlen_batch,
     preset,
     PRESETS,

@@ -289,6 +289,25 @@ VARLEN_PRESETS = {
 }
 
 
+def make_key_block_lists(*, B: int, hkv: int, lp: int, density: float, block_keys: int = 64, seed: int = 0):
+    """Selected and complementary key-block lists for a sparse attention over
+    a prefix of lp keys: per (sequence, KV head), round(density * n) of the
+    n = ceil(lp / block_keys) blocks, chosen uniformly at random (a seeded
+    stand-in for a sparse-attention method's top-k selection), ascending.
+    Returns int32 arrays [B, hkv, k] and [B, hkv, n - k]."""
+    rng = np.random.default_rng(seed)
+    n = (lp + block_keys - 1) // block_keys
+    k = int(round(density * n))
+    sel = np.empty((B, hkv, k), dtype=np.int32)
+    rest = np.empty((B, hkv, n - k), dtype=np.int32)
+    for b in range(B):
+        for g in range(hkv):
+            perm = rng.permutation(n)
+            sel[b, g] = np.sort(perm[:k])
+            rest[b, g] = np.sort(perm[k:])
+    return sel, rest
+
+
 def preset(name: str, **overrides):
     """Build one of the named workloads; keyword overrides replace fields."""
     if name in PRESETS:
