@@ -19,6 +19,8 @@ from .api import (  # noqa: F401
     ba_prefix_attn_workspace,
     ba_reuse_gate,
     ba_reuse_gate_workspace,
+    ba_sparse_prefix_attn,
+    ba_sparse_prefix_attn_workspace,
     ba_split_attn,
     ba_varlen_pack,
     ba_version,

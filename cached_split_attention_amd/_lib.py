@@ -55,6 +55,10 @@ EXPORTS = {
     "ba_prefix_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc)]),
     "ba_prefix_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "ba_sparse_prefix_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc), ctypes.c_int32]),
+    "ba_sparse_prefix_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p]),
     "ba_prefix_attn_merge": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,

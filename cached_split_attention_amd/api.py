@@ -19,7 +19,8 @@ from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_C
 __all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge", "ba_split_attn",
            "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
            "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
-           "ba_debug_set_gate_spin_limit", "BA_GATE_COUNT", "BA_GATE_COSINE"]
+           "ba_debug_set_gate_spin_limit", "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn",
+           "BA_GATE_COUNT", "BA_GATE_COSINE"]
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -142,6 +143,35 @@ def ba_prefix_attn(q, k, v, a_out, l_out, workspace=None, *, q_layout="bshd", kv
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().ba_prefix_attn(ctypes.byref(desc), _ptr(a_out), _ptr(l_out), _ptr(workspace), nbytes,
                                _stream(stream)))
+
+
+def _blocks(blocks, desc):
+    _need_gpu(blocks)
+    if blocks.dtype != torch.int32 or blocks.dim() != 3 or not blocks.is_contiguous() or \
+            tuple(blocks.shape[:2]) != (desc.n_seq, desc.hkv):
+        raise ValueError("blocks must be a contiguous int32 tensor [n_seq, hkv, n_blocks]")
+    return int(blocks.shape[2])
+
+
+def ba_sparse_prefix_attn_workspace(q, k, v, blocks, *, kv_layout="bhsd", scale=None) -> int:
+    desc, _ = _desc(q, k, v, q_layout="bshd", kv_layout=kv_layout, cu_q=None, cu_k=None,
+                    max_q=None, max_k=None, scale=scale, decision=None)
+    return int(lib().ba_sparse_prefix_attn_workspace(ctypes.byref(desc), _blocks(blocks, desc)))
+
+
+def ba_sparse_prefix_attn(q, k, v, blocks, a_out, l_out, workspace=None, *, kv_layout="bhsd",
+                          decision=None, scale=None, stream=None):
+    """Prefix attention over the listed key blocks (blocks: int32 [n_seq, hkv, n_blocks],
+    block j = keys 64j .. 64j+63) into a_out [R, hq, d] / l_out [R, hq]; dense bf16."""
+    desc, rows = _desc(q, k, v, q_layout="bshd", kv_layout=kv_layout, cu_q=None, cu_k=None,
+                       max_q=None, max_k=None, scale=scale, decision=decision)
+    n_blocks = _blocks(blocks, desc)
+    _check_out(a_out, (rows, desc.hq, desc.d), torch.float32, "a_out")
+    _check_out(l_out, (rows, desc.hq), torch.float32, "l_out")
+    _need_gpu(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().ba_sparse_prefix_attn(ctypes.byref(desc), _ptr(blocks), n_blocks, _ptr(a_out), _ptr(l_out),
+                                      _ptr(workspace), nbytes, _stream(stream)))
 
 
 def ba_prefix_attn_merge(q, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None, workspace=None, *,

@@ -523,14 +523,28 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   const int R = p.group * it.nq;
   it.row0 = it.rt * ROWS;
   if (it.row0 >= R) return it;
+  // the key range [kb, ke) counts keys, or list entries in key-block mode
+  const int units = p.kblocks ? p.n_kblocks : it.nk;
   it.kb = it.split * p.chunk;
   // A sequence with no keys at all is finished by split 0 alone (A = 0,
   // L = -inf); otherwise splits past the end have nothing to do.
-  it.mode = (p.mode == kPrefixPartial && it.nk == 0) ? kPrefixFinal : p.mode;
-  if (p.mode == kPrefixPartial && it.kb >= it.nk && !(it.nk == 0 && it.split == 0)) return it;
-  it.ke = min(it.nk, it.kb + p.chunk);
+  it.mode = (p.mode == kPrefixPartial && units == 0) ? kPrefixFinal : p.mode;
+  if (p.mode == kPrefixPartial && it.kb >= units && !(units == 0 && it.split == 0)) return it;
+  it.ke = min(units, it.kb + p.chunk);
   it.valid = true;
   return it;
+}
+
+// Key-block list mode: this lane's entry of the workgroup's list range
+// (entries kb + lane, lane < ke - kb <= 64), clamped into the sequence's
+// blocks so that a bad index can only give a wrong result, never an access
+// outside K/V.  Tile it starts at key readlane(entry, it) * kBlockKeys.
+__device__ __forceinline__ int load_block_entry(const AttnParams& p, const Item& it, int lane) {
+  if (!p.kblocks) return 0;
+  const int64_t base = ((int64_t)it.b * p.hkv + it.kvh) * p.n_kblocks + it.kb;
+  int e = lane < it.ke - it.kb ? p.kblocks[base + lane] : 0;
+  const int last = (it.nk + kBlockKeys - 1) / kBlockKeys - 1;
+  return min(max(e, 0), last);
 }
 
 // Reuse decision of (sequence b, query head h).  Read with agent-scope loads:
@@ -653,7 +667,10 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
       (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
   const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
       (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
-  const Dma dma(kptr, vptr, p.ks1, p.vs1, ke, w, lane);
+  // key-block list mode: tiles are the listed blocks (KTILE == kBlockKeys)
+  const bool listed = p.kblocks != nullptr;
+  const int entry = load_block_entry(p, itm, lane);
+  const Dma dma(kptr, vptr, p.ks1, p.vs1, listed ? itm.nk : ke, w, lane);
   auto issue_tile = [&](int t0, int st) {
     const unsigned kdst = smem_base + st * STAGE_B;
     dma.issue(t0, kdst, kdst + TILE_B);
@@ -685,18 +702,21 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   const float c2 = p.scale_log2;
   const OperandOffsets<D> off(kg * KT, lane);
 
-  auto compute_tile = [&](const unsigned char* sK, const unsigned char* sV, int g0) {
+  auto compute_tile = [&](const unsigned char* sK, const unsigned char* sV, int g0, int g1) {
     f32x16 s[MB];
     u32x4 pk[MB][2];
     score_mfma<D, MB>(s, sK, off, qf);
-    softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, g0, ke, hf);
+    softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, g0, g1, hf);
     pv_mfma<D, MB>(o, pk, sV, off);
   };
 
-  const int n_iter = (ke > kb) ? (ke - kb + KTILE - 1) / KTILE : 0;
+  const int n_iter = listed ? ke - kb : (ke > kb) ? (ke - kb + KTILE - 1) / KTILE : 0;
+  // first key and key bound of tile it
+  auto tile_key = [&](int it) { return listed ? __builtin_amdgcn_readlane(entry, it) * KTILE : kb + it * KTILE; };
+  auto tile_end = [&](int it) { return listed ? min(tile_key(it) + KTILE, itm.nk) : ke; };
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
-    if (s < n_iter) issue_tile(kb + s * KTILE, s);
+    if (s < n_iter) issue_tile(tile_key(s), s);
   wait_vmem_all();
 
   // The loop is unrolled over the ring so each copy reads a fixed stage.
@@ -715,9 +735,9 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
           else if (ahead == 1) wait_barrier<Dma::OPS>();
           else wait_barrier<0>();
         }
-        if (it + ST - 1 < n_iter) issue_tile(kb + (it + ST - 1) * KTILE, (st + ST - 1) % ST);
-        const int g0 = kb + it * KTILE + kg * KT;
-        if (g0 < ke) compute_tile(smem + st * STAGE_B, smem + st * STAGE_B + TILE_B, g0);
+        if (it + ST - 1 < n_iter) issue_tile(tile_key(it + ST - 1), (st + ST - 1) % ST);
+        const int g0 = tile_key(it) + kg * KT, g1 = tile_end(it);
+        if (g0 < g1) compute_tile(smem + st * STAGE_B, smem + st * STAGE_B + TILE_B, g0, g1);
       }
     }
   }
@@ -843,10 +863,15 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
       (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
   const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
       (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
-  const Dma dma(kptr, vptr, p.ks1, p.vs1, ke, w, lane);
+  // key-block list mode: tiles are the listed blocks (KT == kBlockKeys)
+  const bool listed = p.kblocks != nullptr;
+  const int entry = load_block_entry(p, itm, lane);
+  auto tile_key = [&](int u) { return listed ? __builtin_amdgcn_readlane(entry, u) * KT : kb + u * KT; };
+  auto tile_end = [&](int u) { return listed ? min(tile_key(u) + KT, itm.nk) : ke; };
+  const Dma dma(kptr, vptr, p.ks1, p.vs1, listed ? itm.nk : ke, w, lane);
   auto issue_tile = [&](int u) {
     const unsigned kdst = smem_base + (u % NS) * STAGE_B;
-    dma.issue(kb + u * KT, kdst, kdst + TILE_B);
+    dma.issue(tile_key(u), kdst, kdst + TILE_B);
   };
 
   f32x16 o[DB];
@@ -866,7 +891,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   // phase behind.  At every even workgroup phase 2v all waves wait for tile
   // v and issue tile v+2; for group 0 these are the barriers opening its
   // matrix phases, for group 1 those opening its vector phases.
-  const int n = (ke > kb) ? (ke - kb + KT - 1) / KT : 0;
+  const int n = listed ? ke - kb : (ke > kb) ? (ke - kb + KT - 1) / KT : 0;
   auto even_barrier = [&](int v) {
     const int later = min(LOOK - 1, n - 1 - v);   // tiles issued after tile v
     if (later >= 2) phase_barrier<2 * Dma::OPS>();
@@ -883,7 +908,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   if (active && n > 0) score_mfma<D, MB>(s, smem, off, qf);
   for (int u = 0; u < n; ++u) {
     if (grp) even_barrier(u + 1); else phase_barrier<63>();
-    if (active) softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, kb + u * KT, ke, hf);
+    if (active) softmax_tile<D, MB>(s, pk, o, m_run, l_run, c2, tile_key(u), tile_end(u), hf);
     if (grp) phase_barrier<63>(); else even_barrier(u + 1);
     // (after the last tile the scores are computed from a stale stage and
     // never used: one branch-free block keeps the accumulators in place).
@@ -956,12 +981,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     a_c = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
   }
   // An empty prefix is written by the attention kernel's split 0.
-  const bool fresh = p.mode == kPrefixPartial && nk > 0 && !(p.decision && p.decision[b * p.hq + h]);
+  const bool fresh = p.mode == kPrefixPartial && (p.kblocks ? p.n_kblocks : nk) > 0 &&
+                     !(p.decision && p.decision[b * p.hq + h]);
   if (!fresh && !p.a_full) return;
   f32x4 a_o;
   float l_o;
   if (fresh) {
-    const int ns = (nk + p.chunk - 1) / p.chunk;
+    const int units = p.kblocks ? p.n_kblocks : nk;   // keys, or listed key blocks
+    const int ns = (units + p.chunk - 1) / p.chunk;
     const float* la = p.ws_l + e;
     const float* aa = p.ws_a + e * D + 4 * t;
     const int64_t cs = n_entries;

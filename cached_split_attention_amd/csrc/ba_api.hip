@@ -93,7 +93,9 @@ struct PrefixPlan {
   int chunk;
 };
 
-PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
+// n_kblocks >= 0: key-block list mode, one iteration tile per listed block
+// and at most 64 list entries per workgroup; chunk then counts entries.
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
     pp.row_tiles = 1;
@@ -107,7 +109,8 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   if (pp.row_tiles < 1) pp.row_tiles = 1;
   const int64_t items = (int64_t)d->n_seq * d->hkv * pp.row_tiles;
   const int kpi = pp.bf.keys_per_iter;
-  const int64_t iters = (d->max_k + kpi - 1) / kpi;
+  const bool listed = n_kblocks >= 0;
+  const int64_t iters = listed ? n_kblocks : (d->max_k + kpi - 1) / kpi;
   // Pick the key-split count minimising a makespan estimate in units of one
   // iteration tile of one workgroup: (rounds of workgroups over all slots) x
   // (tiles per workgroup + 2 for pipeline fill and epilogue), plus, with
@@ -132,6 +135,12 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group) {
   }
   int64_t chunk_iters = (iters + best_s - 1) / best_s;
   if (chunk_iters < 1) chunk_iters = 1;
+  if (listed) {
+    if (chunk_iters > 64) chunk_iters = 64;
+    pp.chunk = (int)chunk_iters;
+    pp.n_splits = iters > 0 ? (int)((iters + chunk_iters - 1) / chunk_iters) : 1;
+    return pp;
+  }
   pp.chunk = (int)(chunk_iters * kpi);
   pp.n_splits = d->max_k > 0 ? (int)((d->max_k + pp.chunk - 1) / pp.chunk) : 1;
   if (pp.n_splits < 1) pp.n_splits = 1;
@@ -200,7 +209,8 @@ namespace {
 ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
                       const float* l_in, float* a_full, float* l_full, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, ba::AttnParams* block = nullptr,
-                      const ba_attn_desc* block_desc = nullptr, const ba::GateParams* gate = nullptr) {
+                      const ba_attn_desc* block_desc = nullptr, const ba::GateParams* gate = nullptr,
+                      const int32_t* kblocks = nullptr, int n_kblocks = -1) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
@@ -211,7 +221,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
-  const PrefixPlan pp = plan_prefix(desc, sh.group);
+  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1);
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
@@ -224,6 +234,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   p.row_tiles = pp.row_tiles;
   p.a = a_out;
   p.l = l_out;
+  p.kblocks = kblocks;
+  p.n_kblocks = kblocks ? n_kblocks : 0;
   if (gate) {
     p.ready = gate->ready;
     p.ready_stride = gate->ready_stride;
@@ -267,6 +279,51 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
 }
 
 }  // namespace
+
+namespace {
+
+// Key-block list mode is for the dense bf16 prefix kernels.
+ba_status check_sparse(const ba_attn_desc* desc, int32_t n_blocks) {
+  AttnShape sh;
+  const ba_status st = check_desc(desc, &sh);
+  if (st != BA_OK) return st;
+  if (desc->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "key-block lists need bf16");
+  if (desc->cu_q || desc->cu_k) return fail(BA_ERR_UNSUPPORTED, "key-block lists are for dense prefixes");
+  const int64_t n_max = ((int64_t)desc->max_k + ba::kBlockKeys - 1) / ba::kBlockKeys;
+  if (n_blocks < 0 || n_blocks > n_max)
+    return fail(BA_ERR_SHAPE, "n_blocks %d out of [0, %lld]", n_blocks, (long long)n_max);
+  return BA_OK;
+}
+
+}  // namespace
+
+size_t ba_sparse_prefix_attn_workspace(const ba_attn_desc* desc, int32_t n_blocks) {
+  if (check_sparse(desc, n_blocks) != BA_OK) return 0;
+  AttnShape sh;
+  check_desc(desc, &sh);
+  if (n_blocks == 0) {
+    ba_attn_desc e = *desc;
+    e.max_k = 0;
+    return prefix_ws_bytes(&e, plan_prefix(&e, sh.group));
+  }
+  return prefix_ws_bytes(desc, plan_prefix(desc, sh.group, n_blocks));
+}
+
+ba_status ba_sparse_prefix_attn(const ba_attn_desc* desc, const int32_t* blocks, int32_t n_blocks, float* a_out,
+                                float* l_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  const ba_status st = check_sparse(desc, n_blocks);
+  if (st != BA_OK) return st;
+  if (n_blocks == 0) {
+    // no key selected: the attention of an empty key set (A = 0, L = -inf)
+    ba_attn_desc e = *desc;
+    e.max_k = 0;
+    return prefix_impl(&e, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+  }
+  if (!blocks) return fail(BA_ERR_NULL, "blocks is NULL");
+  return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                     nullptr, nullptr, nullptr, blocks, n_blocks);
+}
 
 ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {

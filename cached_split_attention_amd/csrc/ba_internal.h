@@ -53,7 +53,14 @@ struct AttnParams {
   int spin_limit;
   int gate_mode;
   int gate_tau;
+  // Key-block list mode (dense prefix only): (sequence, KV head) attends over
+  // the keys of blocks kblocks[(b*hkv + kvh)*n_kblocks + i], i < n_kblocks,
+  // block j being keys [kBlockKeys*j, kBlockKeys*(j+1)) clipped to max_k;
+  // chunk and the item key ranges then count list entries, not keys.
+  const int32_t* kblocks;
+  int n_kblocks;
 };
+constexpr int kBlockKeys = 64;   // keys per listed key block = the prefix kernels' tile
 
 
 // Launch-shape choice for the bf16 matrix-core kernel.

@@ -112,6 +112,30 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Prefix attention over listed key blocks only, for the sparse-attention
+ * residual reuse of FlashBlock (section 2, "Estrategias de Reutilizacion
+ * Adaptativa", the point on sparse attention; "Contribuciones Clave" 3): the
+ * keys a sparse attention leaves out are treated as the out-of-block set,
+ * whose contribution is computed once and cached, while the selected keys
+ * are attended fresh; the two results are joined by the merge equation
+ * (ba_lse_merge), and merging the results of a list and of its complement
+ * gives ba_prefix_attn over the whole prefix.
+ * Exactly ba_prefix_attn (decision gating, outputs, workspace rules) with
+ * the keys of (sequence b, KV head g) restricted to the blocks
+ *     blocks[(b*hkv + g)*n_blocks + i], i < n_blocks   (device int32),
+ * block j being keys [64*j, min(64*j + 64, max_k)).  Dense bf16 only
+ * (cu_q, cu_k NULL); 0 <= n_blocks <= ceil(max_k / 64).  The indices of one
+ * list must be distinct and in [0, ceil(max_k/64)); this is device data, the
+ * caller's contract: an index out of range is clamped into it (a wrong
+ * result, never an access outside K/V).  n_blocks == 0 gives A = 0,
+ * L = -inf.  The workspace is sized by ba_sparse_prefix_attn_workspace.
+ */
+size_t ba_sparse_prefix_attn_workspace(const ba_attn_desc* desc, int32_t n_blocks);
+ba_status ba_sparse_prefix_attn(const ba_attn_desc* desc, const int32_t* blocks, int32_t n_blocks,
+                                float* a_out, float* l_out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * Prefix attention fused with the log-space merge of FlashBlock "Mecanismo
  * Central", for a step that computes the in-block part first (for example
  * ba_block_attn with a_in/l_in outputs, concurrently with the reuse gate):

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_block_schedule, make_varlen_batch, round_to_bf16_bits
+from workloads import make_block_schedule, make_key_block_lists, make_varlen_batch, round_to_bf16_bits
 from tests.gpu_util import DEV, check_a, check_l, dev_bits, dev_f32, dev_in, host
 
 pytestmark = pytest.mark.gpu
@@ -564,6 +564,91 @@ def test_gated_split_attn_gives_up(mode):
     for nm in ("a_out", "l_out"):
         assert torch.equal(fused[nm][nb:], ref[nm][nb:]), nm
         assert torch.equal(fused[nm][:nb], ref[nm][:nb]), nm
+
+
+SPARSE_SHAPES = [
+    # (B, hq, hkv, d, lp, nb, density): few rows (two key-waves), 128-row
+    # tiles (GQA), the alternating 256-row kernel, d = 64; ragged last
+    # blocks; enough blocks for several list splits (at most 64 per
+    # workgroup); every block listed
+    (2, 4, 4, 128, 64 * 40 + 17, 32, 0.3),
+    (1, 8, 2, 128, 64 * 150, 32, 1.0),
+    (1, 4, 1, 128, 64 * 20 + 1, 80, 0.25),
+    (2, 4, 4, 64, 64 * 9 + 40, 20, 0.5),
+]
+
+
+@pytest.mark.parametrize("shape", SPARSE_SHAPES)
+def test_sparse_prefix_attn(shape):
+    # Prefix attention over a key-block list and over its complement, each
+    # against the oracle on every row, and their merge against attention
+    # over the whole prefix (the residual-reuse identity).
+    B, hq, hkv, d, lp, nb, dens = shape
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=95)
+    sel, rest = make_key_block_lists(B=B, hkv=hkv, lp=lp, density=dens, seed=4)
+    q, kp, vp = dev_in(s.q[0], "bf16"), dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
+    rows = B * nb
+    g = hq // hkv
+    got = {}
+    for nm, lst in (("sel", sel), ("rest", rest)):
+        bl = torch.from_numpy(np.ascontiguousarray(lst)).to(DEV)
+        ws = torch.zeros(max(1, ba.ba_sparse_prefix_attn_workspace(q, kp, vp, bl)), device=DEV, dtype=torch.uint8)
+        a = torch.full((rows, hq, d), 777.0, device=DEV)
+        l = torch.full((rows, hq), 777.0, device=DEV)
+        ba.ba_sparse_prefix_attn(q, kp, vp, bl, a, l, ws)
+        torch.cuda.synchronize()
+        got[nm] = (host(a), host(l))
+        want_a = np.zeros((B, nb, hq, d)); want_l = np.zeros((B, nb, hq))
+        for b in range(B):
+            for h in range(hq):
+                want_a[b, :, h], want_l[b, :, h] = oracle.prefix_rows_in_blocks(s, 0, b, h, lst[b, h // g])
+        if lst.shape[2] == 0:
+            assert np.all(got[nm][0] == 0) and np.all(np.isneginf(got[nm][1]))
+        else:
+            check_a(got[nm][0], want_a.reshape(rows, hq, d), f"A {nm}")
+            check_l(got[nm][1], want_l.reshape(rows, hq), f"L {nm}")
+    am, lm = oracle.merge(got["sel"][0].astype(np.float64), got["sel"][1].astype(np.float64),
+                          got["rest"][0].astype(np.float64), got["rest"][1].astype(np.float64))
+    full_a, full_l = _oracle_prefix(s)
+    check_a(am, full_a, "A merged")
+    check_l(lm, full_l, "L merged")
+
+
+def test_sparse_prefix_attn_gated_and_empty():
+    # The decision gates a listed pass like the dense one (reused heads keep
+    # the cache), and an empty list gives A = 0, L = -inf.
+    B, hq, hkv, d, lp, nb = 2, 4, 4, 128, 64 * 12, 32
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=96)
+    sel, _ = make_key_block_lists(B=B, hkv=hkv, lp=lp, density=0.5, seed=6)
+    q, kp, vp = dev_in(s.q[0], "bf16"), dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
+    rows = B * nb
+    dec = np.array([[1, 0, 1, 0], [0, 0, 1, 1]], dtype=np.uint8)
+    r = np.random.default_rng(3)
+    cache_a = r.standard_normal((rows, hq, d)).astype(np.float32)
+    cache_l = r.standard_normal((rows, hq)).astype(np.float32)
+    a = torch.from_numpy(cache_a).to(DEV)
+    l = torch.from_numpy(cache_l).to(DEV)
+    bl = torch.from_numpy(sel).to(DEV)
+    ws = torch.zeros(max(1, ba.ba_sparse_prefix_attn_workspace(q, kp, vp, bl)), device=DEV, dtype=torch.uint8)
+    ba.ba_sparse_prefix_attn(q, kp, vp, bl, a, l, ws, decision=torch.from_numpy(dec).to(DEV))
+    torch.cuda.synchronize()
+    ga, gl = host(a), host(l)
+    for b in range(B):
+        for h in range(hq):
+            sl = slice(b * nb, (b + 1) * nb)
+            if dec[b, h]:
+                assert np.array_equal(ga[sl, h], cache_a[sl, h]) and np.array_equal(gl[sl, h], cache_l[sl, h])
+            else:
+                wa, wl = oracle.prefix_rows_in_blocks(s, 0, b, h, sel[b, h])
+                check_a(ga[sl, h], wa, f"A b{b} h{h}")
+                check_l(gl[sl, h], wl, f"L b{b} h{h}")
+    empty = torch.zeros(B, hkv, 0, device=DEV, dtype=torch.int32)
+    a0 = torch.full((rows, hq, d), 5.0, device=DEV)
+    l0 = torch.full((rows, hq), 5.0, device=DEV)
+    ws0 = torch.zeros(max(1, ba.ba_sparse_prefix_attn_workspace(q, kp, vp, empty)), device=DEV, dtype=torch.uint8)
+    ba.ba_sparse_prefix_attn(q, kp, vp, empty, a0, l0, ws0)
+    torch.cuda.synchronize()
+    assert torch.all(a0 == 0) and torch.all(torch.isneginf(l0))
 
 
 def test_split_attn_varlen():
