@@ -342,6 +342,142 @@ def run_varlen(args):
     print(json.dumps(out), flush=True)
 
 
+def run_sparse(args, s, q, kps, vps):
+    """Sparse-attention residual reuse on a dense shape: each step attends
+    fresh over a key-block selection (density args.sparse) and merges the
+    result with the cached residual over the unselected blocks (computed
+    once, at a refresh).  Times the selected pass plus the merge (the
+    steady-state prefix part of a step), the residual pass (the refresh) and
+    the dense pass, all with every head recomputing and the prefix copies
+    rotated."""
+    import numpy as np
+    import torch
+    import cached_split_attention_amd as ba
+    from workloads import make_key_block_lists
+    dev = q[1].device
+    sel, rest = make_key_block_lists(B=s.B, hkv=s.hkv, lp=s.lp, density=args.sparse, seed=s.seed + 100)
+    bsel = torch.from_numpy(sel).to(dev)
+    brest = torch.from_numpy(rest).to(dev)
+    rows = s.B * s.nb
+    n_copies = len(kps)
+    bufs = {nm: torch.empty(rows, s.hq, s.d, device=dev) for nm in ("a_sel", "a_res", "a_out", "a_dense")}
+    bufs.update({nm: torch.empty(rows, s.hq, device=dev) for nm in ("l_sel", "l_res", "l_out", "l_dense")})
+    ws_s = torch.zeros(max(1, ba.ba_sparse_prefix_attn_workspace(q[1], kps[0], vps[0], bsel, scale=s.scale)),
+                       device=dev, dtype=torch.uint8)
+    ws_r = torch.zeros(max(1, ba.ba_sparse_prefix_attn_workspace(q[1], kps[0], vps[0], brest, scale=s.scale)),
+                       device=dev, dtype=torch.uint8)
+    ws_d = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q[1], kps[0], vps[0], scale=s.scale)), device=dev,
+                       dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def sparse_step(i, st):
+        ba.ba_sparse_prefix_attn(q[1], kps[i], vps[i], bsel, bufs["a_sel"], bufs["l_sel"], ws_s, scale=s.scale,
+                                 stream=st)
+        ba.ba_lse_merge(bufs["a_sel"], bufs["l_sel"], bufs["a_res"], bufs["l_res"], bufs["a_out"], bufs["l_out"],
+                        stream=st)
+
+    def residual(i, st):
+        ba.ba_sparse_prefix_attn(q[1], kps[i], vps[i], brest, bufs["a_res"], bufs["l_res"], ws_r, scale=s.scale,
+                                 stream=st)
+
+    def dense(i, st):
+        ba.ba_prefix_attn(q[1], kps[i], vps[i], bufs["a_dense"], bufs["l_dense"], ws_d, scale=s.scale, stream=st)
+
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n_copies):
+                    fn(i, torch.cuda.current_stream())
+        stream.wait_stream(side)
+        return g
+
+    residual(0, stream)
+    sparse_step(0, stream)
+    torch.cuda.synchronize()
+    graphs = {nm: graph_of(fn) for nm, fn in (("sparse", sparse_step), ("residual", residual), ("dense", dense))}
+
+    def timed(g, n_rep):
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_rep):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (n_rep * n_copies)
+
+    w0 = time.perf_counter()
+    us = {nm: timed(g, args.steps if nm == "sparse" else 4) for nm, g in graphs.items()}
+    wall = time.perf_counter() - w0
+    # algorithmic bytes: the selected K/V, Q, the partial A/L written, the
+    # cached residual read and A_out/L_out written by the merge
+    es = 2
+    ent = rows * s.hq
+    n_blk = (s.lp + 63) // 64
+    k_sel = int(sel.shape[2])
+    # selected keys summed over (sequence, KV head): a ragged last block counts its own length
+    kv_keys = sum(min(64 * (int(j) + 1), s.lp) - 64 * int(j) for j in sel.reshape(-1))
+    sel_bytes = kv_keys * s.d * es * 2 + ent * s.d * es + ent * (s.d + 1) * 4
+    step_bytes = sel_bytes + 2 * ent * (s.d + 1) * 4
+    sel_flops = 4 * s.d * s.nb * kv_keys * (s.hq // s.hkv)
+    roof, achieved, achieved_tf = roofline_of(sel_bytes, sel_flops, us["sparse"])
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (us["sparse"] * 1e-6) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 1,
+        "ms_per_step": round(us["sparse"] * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic, seeded (workloads.preset, make_key_block_lists), resident in HBM",
+        "config": {"workload": f"{args.workload} with sparse prefix attention: B={s.B} Hq={s.hq} Hkv={s.hkv} "
+                               f"d={s.d} prefix={s.lp}, {k_sel} of {n_blk} 64-key blocks selected per KV head "
+                               f"(density {args.sparse})",
+                   "bench_step": "the prefix part of a sparse step: the pass over the selected blocks, then the "
+                                 "merge with the cached residual; every head recomputes",
+                   "prefix_kv_copies": n_copies},
+        "tflops": round(sel_flops / (us["sparse"] * 1e-6) / 1e12, 4),
+        "latency_us": {"sparse_pass_and_merge": round(us["sparse"], 2), "residual_pass": round(us["residual"], 2),
+                       "dense_pass": round(us["dense"], 2)},
+        "roofline": {"kernel": "selected-block prefix pass + residual merge, back to back", **roof,
+                     "traffic": None, "algorithmic_bytes_per_launch": int(sel_bytes),
+                     "algorithmic_flops_per_launch": int(sel_flops), "gbs": round(achieved, 1),
+                     "tflops": round(achieved_tf, 3)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            threads = 1
+        g = s.hq // s.hkv
+        t0 = time.perf_counter()
+        done = 0
+        for h in range(s.hq):
+            for b in range(s.B):
+                a1, l1 = oracle.prefix_rows_in_blocks(s, 1, b, h, sel[b, h // g])
+                done += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        dt = time.perf_counter() - t0
+        frac = done / (s.B * s.hq)
+        out["cpu_baseline"] = {"value": sel_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"the selected-block pass of {done} of {s.B * s.hq} (sequence, head) pairs, "
+                                         f"bytes scaled to those, NumPy float64, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,6 +488,8 @@ def main():
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated prefix copies")
     ap.add_argument("--lp", type=int, default=None,
                     help="prefix length override for the dense shapes (long-context sweep)")
+    ap.add_argument("--sparse", type=float, default=None,
+                    help="key-block density: time sparse-attention residual reuse instead of the block schedule")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: only the prefix pass, eagerly, over the rotated copies, "
                          "then a plain device copy of known size (the counters' scale reference)")
@@ -392,6 +530,9 @@ def main():
     v = [to_dev(x) for x in s.v]
     if args.probe:
         probe(args, s, q, kps, vps)
+        return
+    if args.sparse is not None:
+        run_sparse(args, s, q, kps, vps)
         return
     attn = ba.CachedBlockAttention(kp0, vp0, nb=s.nb, hq=s.hq, gate=s.gate, tau=s.tau,
                                    gamma=s.gamma, scale=s.scale)
