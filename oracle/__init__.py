@@ -10,6 +10,8 @@ from .reference import (  # noqa: F401
     gate_count,
     head_cosine,
     gate_cosine,
+    kl_rows,
+    lock_update,
     varlen_pack,
     step_gates,
     refresh_steps,

@@ -16,7 +16,9 @@ Sources (gist.science summaries):
         per-head similarity gate gamma for video).
   [SL]  "Resumen Tecnico: SURELOCK" (es/paper/2602.06412), section 2,
         "Accion de Bloqueo" and "Mantenimiento de la Atencion Global": locked
-        tokens issue no queries but stay attended through their cached K/V.
+        tokens issue no queries but stay attended through their cached K/V;
+        "Deteccion de Convergencia": a token locks once the KL divergence of
+        its posterior from the previous step's falls below a threshold.
   [BB]  "Resume Technique : BlockBatch" (fr/paper/2605.29233), "Methodologie",
         "Optimisation Systeme": unmasked query positions of all branches are
         packed into one variable-length buffer.
@@ -198,6 +200,32 @@ def gate_cosine(cos, zero, gamma: float, cache_valid: bool) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # varlen packing of unlocked queries
 # ----------------------------------------------------------------------------
+
+def kl_rows(logits_cur, logits_prev) -> np.ndarray:
+    """Per row, KL(p || q) with p = softmax(cur row), q = softmax(prev row),
+    natural logs, float64.  [SL] Deteccion de Convergencia: D_t = KL(p_t ||
+    p_{t-1}) of each token's posterior over the vocabulary.  Entries with
+    p = 0 contribute 0; q = 0 where p > 0 gives +inf."""
+    x = np.asarray(logits_cur, dtype=np.float64)
+    y = np.asarray(logits_prev, dtype=np.float64)
+    out = np.empty(x.shape[0])
+    for r in range(x.shape[0]):
+        lp = x[r] - x[r].max()
+        lp = lp - math.log(np.exp(lp).sum())
+        lq = y[r] - y[r].max()
+        lq = lq - math.log(np.exp(lq).sum())
+        p = np.exp(lp)
+        with np.errstate(invalid="ignore"):
+            terms = np.where(p > 0, p * (lp - lq), 0.0)
+        out[r] = terms.sum()
+    return out
+
+
+def lock_update(locked, eligible, kl, eps: float) -> np.ndarray:
+    """[SL] Deteccion de Convergencia / Accion de Bloqueo: an eligible token
+    locks once its KL falls below eps, and a locked token stays locked."""
+    return (np.asarray(locked, dtype=bool) | (np.asarray(eligible, dtype=bool) & (kl < eps))).astype(np.uint8)
+
 
 def varlen_pack(locked, block_sizes):
     """Pack the unlocked block positions of all branches into one buffer.

@@ -212,3 +212,30 @@ def test_sparse_residual_split_is_exact():
         assert np.all(a0 == 0) and np.all(np.isneginf(l0))
         ae, le = oracle.merge(a0, l0, af, lf)
         assert np.max(np.abs(ae - af)) < 1e-15 and np.max(np.abs(le - lf)) < 1e-15
+
+
+def test_kl_pins():
+    # [SL] the lock criterion: KL(p || q) of the two steps' posteriors.
+    # Closed forms: identical rows (and a constant shift of a row) give 0;
+    # p = (1/2, 1/2) against q = (1/4, 3/4) gives ln(4/3) / 2; a uniform p
+    # over V against q putting e^c on one entry gives the closed form below;
+    # a zero-probability entry of p adds nothing; q = 0 where p > 0 is +inf.
+    x = np.array([[0.3, -1.2, 2.0, 0.0]])
+    assert abs(oracle.kl_rows(x, x)[0]) < 1e-15
+    assert abs(oracle.kl_rows(x, x + 5.0)[0]) < 1e-14
+    got = oracle.kl_rows(np.array([[0.0, 0.0]]), np.array([[0.0, math.log(3.0)]]))[0]
+    assert abs(got - 0.5 * math.log(4.0 / 3.0)) < 1e-15
+    V, c = 7, 1.7
+    y = np.zeros((1, V)); y[0, 2] = c
+    want = -math.log(V) + math.log(V - 1 + math.exp(c)) - c / V
+    assert abs(oracle.kl_rows(np.zeros((1, V)), y)[0] - want) < 1e-14
+    assert abs(oracle.kl_rows(np.array([[0.0, -np.inf]]), np.array([[0.0, 0.0]]))[0] - math.log(2.0)) < 1e-15
+    assert oracle.kl_rows(np.array([[0.0, 0.0]]), np.array([[0.0, -np.inf]]))[0] == np.inf
+    # Gibbs: KL >= 0, and it grows with the drift of the previous row
+    r = np.random.default_rng(1)
+    a = r.standard_normal((1, 50)) * 3
+    kls = [oracle.kl_rows(a, a + s * r.standard_normal((1, 50)))[0] for s in (0.01, 0.1, 1.0)]
+    assert 0 <= kls[0] < kls[1] < kls[2]
+    # a lock is sticky, and only eligible tokens lock
+    upd = oracle.lock_update([1, 0, 0, 0], [0, 1, 0, 1], np.array([9.0, 0.1, 0.0, 2.0]), 0.5)
+    assert upd.tolist() == [1, 1, 0, 0]

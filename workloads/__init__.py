@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     round_to_bf16_bits,
     make_block_schedule,
     make_key_block_lists,
+    make_logit_pair,
     make_varlen_batch,
     preset,
     PRESETS,

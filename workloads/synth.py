@@ -308,6 +308,23 @@ def make_key_block_lists(*, B: int, hkv: int, lp: int, density: float, block_key
     return sel, rest
 
 
+def make_logit_pair(*, n: int, vocab: int, dtype: str = "bf16", std: float = 3.0,
+                    drift_range=(1e-3, 1.0), seed: int = 0):
+    """Two steps' logits for n token rows over a vocabulary: cur ~ N(0, std^2)
+    i.i.d.; prev = cur + sigma_r * N(0, 1), with a per-row drift sigma_r drawn
+    log-uniformly from drift_range (so the rows span converged and moving
+    tokens).  Returns (cur, prev, sigma) as [n, vocab] arrays (bf16 bit
+    patterns or float32) and the float64 sigmas."""
+    rng = np.random.default_rng(seed)
+    cur = rng.standard_normal((n, vocab), dtype=np.float32) * np.float32(std)
+    lo, hi = math.log(drift_range[0]), math.log(drift_range[1])
+    sigma = np.exp(rng.uniform(lo, hi, size=n))
+    prev = cur + (rng.standard_normal((n, vocab), dtype=np.float32) * sigma[:, None].astype(np.float32))
+    if dtype == "bf16":
+        return round_to_bf16_bits(cur), round_to_bf16_bits(prev), sigma
+    return cur, prev.astype(np.float32), sigma
+
+
 def preset(name: str, **overrides):
     """Build one of the named workloads; keyword overrides replace fields."""
     if name in PRESETS:
