@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     ba_debug_set_gate_spin_limit,
     ba_gated_split_attn,
     ba_gated_split_attn_gate_workspace,
+    ba_kl_lock,
     ba_lse_merge,
     ba_prefix_attn,
     ba_prefix_attn_merge,

@@ -19,7 +19,7 @@ from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_C
 __all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge", "ba_split_attn",
            "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
            "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
-           "ba_debug_set_gate_spin_limit", "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn",
+           "ba_debug_set_gate_spin_limit", "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn", "ba_kl_lock",
            "BA_GATE_COUNT", "BA_GATE_COSINE"]
 
 
@@ -333,6 +333,22 @@ def ba_gated_split_attn(mode, q_prev, kp, vp, k, v, a_out, l_out, a_in, l_in, a_
                                     _ptr(gate_workspace), gbytes, ctypes.byref(dp), ctypes.byref(db),
                                     _ptr(a_out), _ptr(l_out), _ptr(a_in), _ptr(l_in), _ptr(a_full),
                                     _ptr(l_full), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def ba_kl_lock(logits_cur, logits_prev, *, eps, kl=None, locked=None, eligible=None, stream=None):
+    """KL(softmax(cur) || softmax(prev)) per row of [n, vocab] logits into kl (float32 [n]);
+    rows with eligible != 0 (all if None) and KL < eps set locked (uint8 [n]) to 1."""
+    _need_gpu(logits_cur, logits_prev, kl, locked, eligible)
+    if logits_cur.shape != logits_prev.shape or logits_cur.dim() != 2 or logits_cur.dtype != logits_prev.dtype:
+        raise ValueError("logits_cur and logits_prev must be [n, vocab] tensors of one dtype")
+    if logits_cur.stride(1) != 1 or logits_prev.stride(1) != 1 or logits_cur.stride(0) != logits_prev.stride(0):
+        raise ValueError("logit rows must be contiguous with one row stride")
+    n, vocab = logits_cur.shape
+    _check_out(kl, (n,), torch.float32, "kl")
+    _check_out(locked, (n,), torch.uint8, "locked")
+    _check_out(eligible, (n,), torch.uint8, "eligible")
+    check(lib().ba_kl_lock(n, vocab, _dtype(logits_cur), _ptr(logits_cur), _ptr(logits_prev), logits_cur.stride(0),
+                           _ptr(eligible), float(eps), _ptr(kl), _ptr(locked), _stream(stream)))
 
 
 def ba_varlen_pack(block_sizes, locked, cu_seqlens_q, gather_idx, total, q_src=None, q_packed=None,

@@ -566,6 +566,33 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
   return split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &gp);
 }
 
+ba_status ba_kl_lock(int32_t n, int64_t vocab, int32_t dtype, const void* logits_cur, const void* logits_prev,
+                     int64_t row_stride, const uint8_t* eligible, float eps, float* kl, uint8_t* locked,
+                     hipStream_t stream) {
+  g_err.clear();
+  if (n < 0 || vocab < 1) return fail(BA_ERR_SHAPE, "n %d and vocab %lld", n, (long long)vocab);
+  if (dtype != BA_BF16 && dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (row_stride < vocab) return fail(BA_ERR_SHAPE, "row_stride %lld < vocab %lld", (long long)row_stride,
+                                      (long long)vocab);
+  if (!kl && !locked) return fail(BA_ERR_NULL, "no output given (kl and locked are both NULL)");
+  if (n == 0) return BA_OK;
+  if (!logits_cur || !logits_prev) return fail(BA_ERR_NULL, "logits_cur and logits_prev are required");
+  if (!(eps >= 0.0f)) return fail(BA_ERR_SHAPE, "eps must be >= 0");
+  ba::KlParams p{};
+  p.n = n;
+  p.vocab = vocab;
+  p.stride = row_stride;
+  p.esize = esize_of(dtype);
+  p.vec = aligned16(logits_cur) && aligned16(logits_prev) && (row_stride * p.esize) % 16 == 0 ? 1 : 0;
+  p.cur = logits_cur;
+  p.prev = logits_prev;
+  p.eligible = eligible;
+  p.eps = eps;
+  p.kl = kl;
+  p.locked = locked;
+  return hip_status(ba::launch_kl_lock(p, stream), "kl lock");
+}
+
 ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host, const uint8_t* locked,
                          int32_t* cu_seqlens_q, int32_t* gather_idx, int32_t* total, int32_t dtype, int32_t h,
                          int32_t d, const void* q_src, const int64_t q_src_stride[2], void* q_packed,

@@ -129,6 +129,22 @@ int gate_cos_chunks(int n_blk, int d);
 size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d);
 hipError_t launch_gate(const GateParams& p, hipStream_t s);
 
+// KL lock criterion: one row per token, both steps' logits over the vocabulary.
+struct KlParams {
+  int n;                  // token rows
+  int64_t vocab;
+  int64_t stride;         // elements between rows
+  int esize;              // 2 (bf16) or 4 (float32)
+  int vec;                // 1 if rows start 16-byte aligned (vector loads)
+  const void* cur;
+  const void* prev;
+  const uint8_t* eligible;
+  float eps;
+  float* kl;
+  uint8_t* locked;
+};
+hipError_t launch_kl_lock(const KlParams& p, hipStream_t s);
+
 constexpr int kMaxBranches = 512;
 struct PackParams {
   int n_branch;

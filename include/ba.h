@@ -269,6 +269,28 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Lock criterion of SURELOCK ("Deteccion de Convergencia"): for each of n
+ * token rows, the KL divergence of the token's current posterior over the
+ * vocabulary from the previous step's,
+ *     kl[r] = KL(p || q),  p = softmax(logits_cur[r, :]), q = softmax(logits_prev[r, :]),
+ * with natural logs; a row with eligible[r] != 0 (or every row, if eligible
+ * is NULL) locks once kl[r] < eps: locked[r] is set to 1, and never cleared
+ * (a locked token stays locked).  The lock flags feed ba_varlen_pack.
+ *   logits_cur, logits_prev: device [n, vocab] of dtype (bf16 or float32),
+ *     rows row_stride elements apart (row_stride >= vocab).  A -inf logit is
+ *     allowed (that entry has probability 0); a row whose q is 0 where p is
+ *     not has KL = +inf.
+ *   kl: optional device float32 [n]; locked: optional device uint8 [n]
+ *     (read and written); at least one must be given.
+ * Sums are accumulated in float64 from float32 exponentials; the result is
+ * reproducible and within about 1e-6 of the exact KL for vocabularies of a
+ * few hundred thousand entries.
+ */
+ba_status ba_kl_lock(int32_t n, int64_t vocab, int32_t dtype, const void* logits_cur,
+                     const void* logits_prev, int64_t row_stride, const uint8_t* eligible,
+                     float eps, float* kl, uint8_t* locked, hipStream_t stream);
+
+/*
  * Varlen packing of unlocked query positions across branches (BlockBatch
  * "Optimisation Systeme"; SURELOCK "Accion de Bloqueo").  Branch b owns block
  * positions sum(block_sizes_host[:b]) .. ; a position with locked[p] != 0

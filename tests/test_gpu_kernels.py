@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_block_schedule, make_key_block_lists, make_varlen_batch, round_to_bf16_bits
+from workloads import (make_block_schedule, make_key_block_lists, make_logit_pair, make_varlen_batch,
+                       round_to_bf16_bits)
 from tests.gpu_util import DEV, check_a, check_l, dev_bits, dev_f32, dev_in, host
 
 pytestmark = pytest.mark.gpu
@@ -649,6 +650,80 @@ def test_sparse_prefix_attn_gated_and_empty():
     ba.ba_sparse_prefix_attn(q, kp, vp, empty, a0, l0, ws0)
     torch.cuda.synchronize()
     assert torch.all(a0 == 0) and torch.all(torch.isneginf(l0))
+
+
+KL_SHAPES = [
+    # (n rows, vocab, dtype, extra row padding): vector loads with and
+    # without a ragged tail, float32, a large vocabulary, and rows whose
+    # stride breaks 16-byte alignment (scalar loads)
+    (37, 1000, "bf16", 0),
+    (64, 4099, "bf16", 0),
+    (16, 2050, "f32", 0),
+    (5, 126464, "bf16", 0),
+    (9, 777, "bf16", 3),
+]
+
+
+@pytest.mark.parametrize("shape", KL_SHAPES)
+def test_kl_lock(shape):
+    # KL of each row's current posterior from the previous step's against the
+    # oracle, and the lock update (eligible rows below eps lock; locks stay).
+    n, vocab, dtype, pad = shape
+    cur, prev, _ = make_logit_pair(n=n, vocab=vocab, dtype=dtype, seed=n + vocab)
+    want = oracle.kl_rows(oracle.to_f64(cur, dtype), oracle.to_f64(prev, dtype))
+
+    def dev(x):
+        t = dev_in(x, dtype)
+        if pad:
+            big = torch.zeros(n, vocab + pad, device=DEV, dtype=t.dtype)
+            big[:, :vocab] = t
+            return big[:, :vocab]
+        return t
+
+    xc, xp = dev(cur), dev(prev)
+    eps = float(np.median(want))
+    r = np.random.default_rng(n)
+    eligible = (r.random(n) < 0.8).astype(np.uint8)
+    locked0 = (r.random(n) < 0.2).astype(np.uint8)
+    kl = torch.full((n,), -1.0, device=DEV)
+    locked = torch.from_numpy(locked0.copy()).to(DEV)
+    ba.ba_kl_lock(xc, xp, eps=eps, kl=kl, locked=locked, eligible=torch.from_numpy(eligible).to(DEV))
+    torch.cuda.synchronize()
+    got = host(kl).astype(np.float64)
+    tol = 2e-6 + 1e-5 * want
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), f"KL off at rows {np.flatnonzero(bad)[:5]}: {got[bad][:5]} vs {want[bad][:5]}"
+    exp_lock = oracle.lock_update(locked0, eligible, want, eps)
+    gl = host(locked)
+    near = np.abs(want - eps) <= tol
+    assert np.array_equal(gl[~near], exp_lock[~near])
+    assert near.sum() <= 1   # the median row itself may sit on the threshold
+
+
+def test_kl_lock_edge_values():
+    # -inf logits (zero-probability entries), a q with zero mass where p has
+    # some (KL = +inf: never locks), identical rows (KL = 0), and kl-only /
+    # lock-only calls.
+    vocab = 300
+    cur, prev, _ = make_logit_pair(n=4, vocab=vocab, dtype="f32", seed=8)
+    cur = cur.copy(); prev = prev.copy()
+    cur[0, :50] = -np.inf; prev[0, :50] = -np.inf
+    prev[1, 7] = -np.inf
+    prev[2] = cur[2]
+    cur[3, 100:] = -np.inf
+    want = oracle.kl_rows(cur, prev)
+    assert np.isinf(want[1]) and want[2] == 0
+    xc, xp = torch.from_numpy(cur).to(DEV), torch.from_numpy(prev).to(DEV)
+    kl = torch.empty(4, device=DEV)
+    ba.ba_kl_lock(xc, xp, eps=1e-3, kl=kl)
+    locked = torch.zeros(4, device=DEV, dtype=torch.uint8)
+    ba.ba_kl_lock(xc, xp, eps=1e-3, locked=locked)
+    torch.cuda.synchronize()
+    got = host(kl).astype(np.float64)
+    assert np.isinf(got[1]) and got[2] == 0
+    for r_ in (0, 3):
+        assert abs(got[r_] - want[r_]) <= 2e-6 + 1e-5 * want[r_]
+    assert host(locked).tolist() == [int(want[0] < 1e-3), 0, 1, int(want[3] < 1e-3)]
 
 
 def test_split_attn_varlen():
