@@ -16,7 +16,9 @@ Prints one JSON line.  value = algorithmic bytes moved per second (GB/s);
 TFLOP/s, per-step latencies, the prefix kernel's roofline and the CPU
 oracle's rate on a bounded sample ride along.  --workload selects another of
 the workload shapes; the multi-branch varlen one (c5_varlen) times one step
-with a cold cache (varlen packing, then the split attention).
+with a cold cache (varlen packing, then the split attention); kl_lock times
+the lock criterion; --lp and --sparse give the long-context and sparse
+residual-reuse legs of the dense shapes.
 """
 
 from __future__ import annotations
@@ -478,6 +480,85 @@ def run_sparse(args, s, q, kps, vps):
     print(json.dumps(out), flush=True)
 
 
+KL_ROWS, KL_VOCAB = 252, 126464   # the varlen batch's block positions; a vocabulary size chosen here
+
+
+def run_kl(args):
+    """The lock criterion on its own: KL of each token's posterior from the
+    previous step's over a 126464-entry vocabulary, for the 252 block
+    positions of the multi-branch varlen batch, bf16 logits, with the lock
+    update; logit copies rotated over at least args.cold_bytes GiB so the
+    rows come from HBM."""
+    import numpy as np
+    import torch
+    import cached_split_attention_amd as ba
+    from workloads import make_logit_pair
+    dev = torch.device("cuda:0")
+    cur, prev, _ = make_logit_pair(n=KL_ROWS, vocab=KL_VOCAB, dtype="bf16", seed=7)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    c0, p0 = to_dev(cur), to_dev(prev)
+    pair_bytes = 2 * c0.numel() * 2
+    n_copies = max(1, int(math.ceil(args.cold_bytes * (1 << 30) / pair_bytes)))
+    cs = [c0] + [c0.clone() for _ in range(n_copies - 1)]
+    ps = [p0] + [p0.clone() for _ in range(n_copies - 1)]
+    kl = torch.empty(KL_ROWS, device=dev)
+    locked = torch.zeros(KL_ROWS, device=dev, dtype=torch.uint8)
+    eps = 1e-3
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n_copies):
+                ba.ba_kl_lock(cs[i], ps[i], eps=eps, kl=kl, locked=locked, stream=torch.cuda.current_stream())
+    stream.wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    us = e0.elapsed_time(e1) * 1e3 / (args.steps * n_copies)
+    nbytes = pair_bytes + KL_ROWS * (4 + 1 + 1)
+    roof, achieved, _ = roofline_of(nbytes, 1, us)
+    out = {
+        "metric": METRIC, "value": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 1, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic, seeded (workloads.make_logit_pair), resident in HBM",
+        "config": {"workload": f"kl_lock: {KL_ROWS} token rows x {KL_VOCAB} vocabulary entries, two steps' bf16 "
+                               f"logits, eps {eps}",
+                   "bench_step": "one lock-criterion pass (KL per row and the lock update)",
+                   "copies": n_copies},
+        "latency_us": {"kl_pass": round(us, 2)},
+        "roofline": {"kernel": "kl_lock_kernel", **roof, "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            threads = 1
+        rows = 64
+        t0 = time.perf_counter()
+        oracle.kl_rows(oracle.to_f64(cur[:rows], "bf16"), oracle.to_f64(prev[:rows], "bf16"))
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": nbytes * rows / KL_ROWS / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"{rows} of {KL_ROWS} rows, NumPy float64, {dt:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -502,6 +583,9 @@ def main():
     from workloads.synth import VARLEN_PRESETS
     if args.workload in VARLEN_PRESETS:
         run_varlen(args)
+        return
+    if args.workload == "kl_lock":
+        run_kl(args)
         return
 
     import numpy as np

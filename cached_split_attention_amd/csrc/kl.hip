@@ -5,12 +5,25 @@
 // and a token that may be locked locks once D < eps; a locked token stays
 // locked.  One workgroup per token row streams both logit rows once:
 //     KL = sum_i p_i (x_i - y_i) - (LSE(x) - LSE(y))
-//        = S / Z_x - (m_x + log Z_x) + (m_y + log Z_y)
-// with Z_x = sum e^{x_i - m_x}, S = sum e^{x_i - m_x} (x_i - y_i) and Z_y
-// likewise over y, kept per thread with running maxima (exponentials in
-// float32 with the accurate expf, sums in float64) and reduced over the
-// workgroup in a fixed order, so the result is bitwise reproducible.
+//        = S / Z_x - LSE(x) + LSE(y)
+// with Z_x = sum 2^(c x_i - m_x), S = sum 2^(c x_i - m_x) (x_i - y_i) and Z_y
+// likewise over y, c = log2(e) rounded to float32, m a shift per thread.
+//
+// Numerics.  Each term is one float32 fma and one hardware exp2, so every
+// term is exp((1 + e) x_i - m ln 2) with one common e = c / log2(e) - 1
+// (|e| < 2^-24) and its own rounding; with LSE = m ln 2 + ln Z and S / Z
+// scaled by c / log2(e) in float64, the result is the exact KL of the logits
+// scaled by 1 + e, up to the rounding of the terms and sums.  The shift m is
+// not a running maximum: a thread keeps its shift until a chunk's terms sum
+// past 2^64 (or a term is not finite), and only then takes the chunk's
+// maximum as the new shift, rescales its sums and redoes the chunk with the
+// guards that -inf logits need (a zero-weight term adds nothing to S even
+// where x - y is not finite).  Terms are summed per 8-element chunk in
+// float32 and the chunk sums added in float64; the workgroup reduces under
+// its largest shift in float64 in a fixed order, so the result is bitwise
+// reproducible.
 
+#include <float.h>
 #include <math.h>
 
 #include "ba_internal.h"
@@ -23,13 +36,13 @@ constexpr int kKlThreads = 512;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct KlPart {
-  float mx, my;   // running maxima (log space)
+  float mx, my;   // shifts (log2 units)
   double zx, s, zy;
 };
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short u) { return __uint_as_float((unsigned)u << 16); }
 
-// Loads 8 consecutive logits of a row as float32 (16-byte loads for bf16,
+// Loads 8 consecutive logits of a row as float32 (one 16-byte load for bf16,
 // two for float32).
 template <typename T>
 __device__ __forceinline__ void load8(const T* row, int64_t i, float (&o)[8]) {
@@ -57,44 +70,67 @@ __device__ __forceinline__ float load1(const T* row, int64_t i) {
   else return row[i];
 }
 
-// Adds elements x[0..n) / y[0..n) to the running part.
-__device__ __forceinline__ void accumulate(KlPart& a, const float* x, const float* y, int n) {
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kChunkLimit = 0x1p64f;   // a chunk sum above this moves the shift
+
+// Guarded step: new shifts from the chunk's maxima where they exceed the
+// current ones (sums rescaled in float64), then the chunk's terms.
+__device__ __forceinline__ void accumulate_guarded(KlPart& a, const float* x, const float* y, int n) {
   float cx = -INFINITY, cy = -INFINITY;
   for (int j = 0; j < n; ++j) {
     cx = fmaxf(cx, x[j]);
     cy = fmaxf(cy, y[j]);
   }
-  if (cx > a.mx) {
-    const double r = (double)expf(a.mx - cx);   // 0 when the old max is -inf
+  const float nx = cx * kLog2e, ny = cy * kLog2e;
+  if (nx > a.mx) {
+    const double r = a.mx == -INFINITY ? 0.0 : exp2((double)a.mx - (double)nx);
     a.zx *= r;
     a.s *= r;
-    a.mx = cx;
+    a.mx = nx;
   }
-  if (cy > a.my) {
-    a.zy *= (double)expf(a.my - cy);
-    a.my = cy;
+  if (ny > a.my) {
+    a.zy *= a.my == -INFINITY ? 0.0 : exp2((double)a.my - (double)ny);
+    a.my = ny;
   }
+  // a shift still at -inf (every logit so far -inf) is used as -FLT_MAX so
+  // that the terms come out 0, not NaN
+  const float mx = fmaxf(a.mx, -FLT_MAX), my = fmaxf(a.my, -FLT_MAX);
+  float zx = 0.0f, sx = 0.0f, zy = 0.0f;
   for (int j = 0; j < n; ++j) {
-    // (a running max still at -inf means every term so far has weight 0)
-    const float ex = a.mx == -INFINITY ? 0.0f : expf(x[j] - a.mx);
-    a.zx += ex;
-    // a zero-weight term adds nothing even where x - y is not finite
-    if (ex > 0.0f) a.s += (double)ex * ((double)x[j] - (double)y[j]);
-    a.zy += a.my == -INFINITY ? 0.0f : expf(y[j] - a.my);
+    const float ex = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -mx));
+    zx += ex;
+    if (ex > 0.0f) sx = fmaf(ex, x[j] - y[j], sx);
+    zy += __builtin_amdgcn_exp2f(fmaf(y[j], kLog2e, -my));
+  }
+  a.zx += zx;
+  a.s += sx;
+  a.zy += zy;
+}
+
+// Fast step under the current shifts; falls back to the guarded step when
+// the chunk overflows the limit or yields a NaN (the first chunk always
+// does: the shifts start at -inf).
+__device__ __forceinline__ void accumulate8(KlPart& a, const float (&x)[8], const float (&y)[8]) {
+  float zx = 0.0f, sx = 0.0f, zy = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float ex = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -a.mx));
+    zx += ex;
+    sx = fmaf(ex, x[j] - y[j], sx);
+    zy += __builtin_amdgcn_exp2f(fmaf(y[j], kLog2e, -a.my));
+  }
+  if (zx <= kChunkLimit && zy <= kChunkLimit && sx == sx) {
+    a.zx += zx;
+    a.s += sx;
+    a.zy += zy;
+  } else {
+    accumulate_guarded(a, x, y, 8);
   }
 }
 
-__device__ __forceinline__ void combine(KlPart& a, const KlPart& b) {
-  const float mx = fmaxf(a.mx, b.mx), my = fmaxf(a.my, b.my);
-  const double ra = a.mx == -INFINITY ? 0.0 : (double)expf(a.mx - mx);
-  const double rb = b.mx == -INFINITY ? 0.0 : (double)expf(b.mx - mx);
-  a.zx = a.zx * ra + b.zx * rb;
-  a.s = a.s * ra + b.s * rb;
-  a.mx = mx;
-  const double qa = a.my == -INFINITY ? 0.0 : (double)expf(a.my - my);
-  const double qb = b.my == -INFINITY ? 0.0 : (double)expf(b.my - my);
-  a.zy = a.zy * qa + b.zy * qb;
-  a.my = my;
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const int lo = __shfl_xor(__double2loint(v), m), hi = __shfl_xor(__double2hiint(v), m);
+  return __hiloint2double(hi, lo);
 }
 
 template <typename T>
@@ -106,47 +142,84 @@ __global__ void __launch_bounds__(kKlThreads) kl_lock_kernel(const KlParams p) {
   KlPart a{-INFINITY, -INFINITY, 0.0, 0.0, 0.0};
   const int64_t V = p.vocab;
   if (p.vec) {
-    // 8 logits per load, 4 loads of each row in flight per thread
+    // 8 logits per chunk, KU chunks of each row loaded before any is summed;
+    // every load is issued (a chunk past the end re-reads the last one and
+    // is not summed), so the loads are not split by waits.
+    constexpr int KU = 4;
     const int64_t n8 = V / 8;
-    for (int64_t c0 = t; c0 < n8; c0 += 4 * kKlThreads) {
-      float xs[4][8], ys[4][8];
-      int cnt = 0;
+    for (int64_t c0 = t; c0 < n8; c0 += KU * kKlThreads) {
+      float xs[KU][8], ys[KU][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t c = c0 + (int64_t)u * kKlThreads;
-        if (c < n8) {
-          load8(x, c * 8, xs[u]);
-          load8(y, c * 8, ys[u]);
-          cnt = u + 1;
-        }
+      for (int u = 0; u < KU; ++u) {
+        const int64_t c = min(c0 + (int64_t)u * kKlThreads, n8 - 1);
+        load8(x, c * 8, xs[u]);
+        load8(y, c * 8, ys[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < cnt) accumulate(a, xs[u], ys[u], 8);
+      for (int u = 0; u < KU; ++u)
+        if (c0 + (int64_t)u * kKlThreads < n8) accumulate8(a, xs[u], ys[u]);
     }
     for (int64_t i = n8 * 8 + t; i < V; i += kKlThreads) {
       const float xv = load1(x, i), yv = load1(y, i);
-      accumulate(a, &xv, &yv, 1);
+      accumulate_guarded(a, &xv, &yv, 1);
     }
   } else {
     for (int64_t i = t; i < V; i += kKlThreads) {
       const float xv = load1(x, i), yv = load1(y, i);
-      accumulate(a, &xv, &yv, 1);
+      accumulate_guarded(a, &xv, &yv, 1);
     }
   }
-  // fixed-order tree over the workgroup
-  __shared__ KlPart red[kKlThreads];
-  red[t] = a;
-  __syncthreads();
-  for (int s = kKlThreads / 2; s > 0; s >>= 1) {
-    if (t < s) combine(red[t], red[t + s]);
-    __syncthreads();
+  // Workgroup reduction: the largest shifts (wave shuffles, then the waves
+  // in order), every thread's sums rescaled to them in float64, then summed
+  // by an xor butterfly per wave (the same value in every lane) and the
+  // waves' sums added in wave order.
+  constexpr int kWaves = kKlThreads / 64;
+  __shared__ float s_mx[kWaves], s_my[kWaves];
+  __shared__ double s_sum[3][kWaves];
+  const int w = t >> 6, lane = t & 63;
+  float mx = a.mx, my = a.my;
+  for (int m = 32; m > 0; m >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, m));
+    my = fmaxf(my, __shfl_xor(my, m));
   }
+  if (lane == 0) {
+    s_mx[w] = mx;
+    s_my[w] = my;
+  }
+  __syncthreads();
+  mx = s_mx[0];
+  my = s_my[0];
+  for (int i = 1; i < kWaves; ++i) {
+    mx = fmaxf(mx, s_mx[i]);
+    my = fmaxf(my, s_my[i]);
+  }
+  const double r = a.mx == -INFINITY ? 0.0 : exp2((double)a.mx - (double)mx);
+  const double q = a.my == -INFINITY ? 0.0 : exp2((double)a.my - (double)my);
+  double zx = a.zx * r, sxy = a.s * r, zy = a.zy * q;
+  for (int m = 1; m < 64; m <<= 1) {
+    zx += shfl_xor_f64(zx, m);
+    sxy += shfl_xor_f64(sxy, m);
+    zy += shfl_xor_f64(zy, m);
+  }
+  if (lane == 0) {
+    s_sum[0][w] = zx;
+    s_sum[1][w] = sxy;
+    s_sum[2][w] = zy;
+  }
+  __syncthreads();
   if (t != 0) return;
-  const KlPart r = red[0];
-  const double lse_x = (double)r.mx + log(r.zx);
-  const double lse_y = (double)r.my + log(r.zy);
-  double kl = r.s / r.zx - lse_x + lse_y;
+  zx = s_sum[0][0];
+  sxy = s_sum[1][0];
+  zy = s_sum[2][0];
+  for (int i = 1; i < kWaves; ++i) {
+    zx += s_sum[0][i];
+    sxy += s_sum[1][i];
+    zy += s_sum[2][i];
+  }
+  const double kLn2 = 0.69314718055994530942;
+  const double lse_x = (double)mx * kLn2 + log(zx);
+  const double lse_y = (double)my * kLn2 + log(zy);
+  double kl = ((double)kLog2e / 1.44269504088896340736) * (sxy / zx) - lse_x + lse_y;
   if (kl < 0.0) kl = 0.0;   // rounding below the exact minimum of 0
   if (p.kl) p.kl[row] = (float)kl;
   if (p.locked) {

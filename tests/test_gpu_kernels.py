@@ -726,6 +726,47 @@ def test_kl_lock_edge_values():
     assert host(locked).tolist() == [int(want[0] < 1e-3), 0, 1, int(want[3] < 1e-3)]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kl_lock_shift_paths(dtype):
+    # Rows that move a thread's shift after its first chunk or need the
+    # guarded step: a rising ramp over 120 nats (the maximum arrives last),
+    # a falling one, a late spike far above the rest, a leading run of -inf
+    # in both rows, -inf runs in one row only, and logits near the float32
+    # exponential's range; vocabulary with a ragged tail.
+    vocab = 8 * 1024 + 5
+    r = np.random.default_rng(11)
+    cur = r.normal(0.0, 3.0, (8, vocab))
+    prev = cur + r.normal(0.0, 0.05, (8, vocab))
+    ramp = np.linspace(-60.0, 60.0, vocab)
+    cur[0] = ramp + r.normal(0.0, 0.5, vocab)
+    prev[0] = ramp + r.normal(0.0, 0.5, vocab)
+    cur[1] = ramp[::-1] + r.normal(0.0, 0.5, vocab)
+    prev[1] = ramp[::-1] + r.normal(0.0, 0.5, vocab)
+    cur[2, vocab - 700] += 90.0
+    prev[2, vocab - 650] += 88.0
+    cur[3, :3000] = -np.inf
+    prev[3, :3000] = -np.inf
+    cur[4, 100:5000:3] = -np.inf
+    cur[5] += 75.0
+    prev[5] += 70.0
+    cur[6] *= 12.0
+    prev[6] *= 12.0
+    if dtype == "bf16":
+        # (round to nearest even keeps the -inf bit patterns)
+        cur, prev = round_to_bf16_bits(cur.astype(np.float32)), round_to_bf16_bits(prev.astype(np.float32))
+    else:
+        cur, prev = cur.astype(np.float32), prev.astype(np.float32)
+    want = oracle.kl_rows(oracle.to_f64(cur, dtype), oracle.to_f64(prev, dtype))
+    assert np.all(np.isfinite(want))
+    kl = torch.full((8,), -1.0, device=DEV)
+    ba.ba_kl_lock(dev_in(cur, dtype), dev_in(prev, dtype), eps=1e-3, kl=kl)
+    torch.cuda.synchronize()
+    got = host(kl).astype(np.float64)
+    tol = 2e-6 + 1e-5 * want
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), f"KL off at rows {np.flatnonzero(bad)}: {got[bad]} vs {want[bad]}"
+
+
 def test_split_attn_varlen():
     # Branches of different block sizes and prefix lengths (one prefix
     # empty), locked positions packed out, in one varlen split-attention call.
