@@ -38,6 +38,7 @@ METRIC = "block-attn step TFLOP/s + KV GB/s (% of MI355X roofline); per-step lat
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["cached_split_attention_amd/csrc/attn_bf16.hip"]
+KL_SOURCES = ["cached_split_attention_amd/csrc/kl.hip"]
 
 
 # ----------------------------------------------------------------------------
@@ -92,18 +93,19 @@ def varlen_work(vb, total):
 # measured HBM traffic of the prefix kernel (rocprofv3 counters), if current
 # ----------------------------------------------------------------------------
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """Per-launch HBM bytes of the prefix kernel from the committed counter
+def measured_traffic(workload, name=None, sources=KERNEL_SOURCES):
+    """Per-launch HBM bytes of the prefix kernel (or of the kernel whose
+    summary is profiles/<name>_traffic.md) from the committed counter
     summary, or None if absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"prefix_attn_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{name or 'prefix_attn_' + workload}_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -111,7 +113,7 @@ def measured_traffic(workload):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -507,6 +509,18 @@ def run_kl(args):
     kl = torch.empty(KL_ROWS, device=dev)
     locked = torch.zeros(KL_ROWS, device=dev, dtype=torch.uint8)
     eps = 1e-3
+    if args.probe:
+        for i in range(2 * n_copies):
+            ba.ba_kl_lock(cs[i % n_copies], ps[i % n_copies], eps=eps, kl=kl, locked=locked)
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_PROBE_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": args.workload, "kl_passes": 2 * n_copies,
+                          "copy_bytes_each": COPY_PROBE_BYTES, "copies": 4}), flush=True)
+        return
     stream = torch.cuda.current_stream()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -539,7 +553,9 @@ def run_kl(args):
                    "bench_step": "one lock-criterion pass (KL per row and the lock update)",
                    "copies": n_copies},
         "latency_us": {"kl_pass": round(us, 2)},
-        "roofline": {"kernel": "kl_lock_kernel", **roof, "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "roofline": {"kernel": "kl_lock_kernel", **roof,
+                     "traffic": measured_traffic(None, "kl_lock", KL_SOURCES),
+                     "algorithmic_bytes_per_launch": nbytes},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
