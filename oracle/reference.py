@@ -36,7 +36,10 @@ Readings of points the pages leave open (each is listed in the design notes):
   count < tau, or iff cosine > gamma (ties recompute); the first step of a
   block always recomputes; the cosine is that of the head's whole block Q
   (Nb*d values) against the previous step's, a zero norm recomputes; packing
-  is branch-major with ascending position.
+  is branch-major with ascending position.  Gate variants the pages leave
+  open: a count of the positions updated since the last refresh (not only
+  into this step); a partial refresh that recomputes exactly the rows whose Q
+  changed.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 mpmath brute force, the split/merge identity, integer schedules, hand-derived
@@ -161,6 +164,49 @@ def gate_count(m_count, tau: int, cache_valid: bool, hq: int) -> np.ndarray:
     return np.repeat(reuse[:, None], hq, axis=1).astype(np.uint8)
 
 
+def cumulative_gates(changed, tau: int, hq: int):
+    """Count gate on the positions updated since the cache was last written.
+
+    [FB] Estrategias de Reutilizacion Adaptativa gates on a count of updated
+    tokens; this is the variant where the count runs from the last refresh
+    instead of the previous step (a reading the pages leave open).  Written
+    from the definition: at step t, with r the latest step before t whose
+    gate recomputed sequence b (none: r = 0), M_b(t) = the number of
+    positions updated at any step s with r < s <= t; reuse iff the cache is
+    valid (t > 1) and M_b(t) < tau.
+
+    changed: list indexed by step t = 1..S (entry 0 unused) of bool [B, Nb],
+    the positions updated in the transition into step t.  Returns a list
+    indexed the same way of dicts with 'm' (int32 [B]) and 'decision'
+    (uint8 [B, Hq]).
+    """
+    steps = len(changed) - 1
+    B = changed[1].shape[0]
+    out = [None]
+    for t in range(1, steps + 1):
+        m = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            r = 0
+            for s_ in range(1, t):
+                if out[s_]["decision"][b, 0] == 0:
+                    r = s_
+            union = np.zeros(changed[t].shape[1], dtype=bool)
+            for s_ in range(r + 1, t + 1):
+                union |= changed[s_][b]
+            m[b] = int(union.sum())
+        out.append(dict(m=m, decision=gate_count(m, tau, t > 1, hq)))
+    return out
+
+
+def rows_changed(q_cur, q_prev) -> np.ndarray:
+    """Per sequence, the block positions whose Q row (any head) changed
+    bitwise: the rows whose out-of-block part a partial refresh recomputes.
+    A row's A_out/L_out depend only on its own query and the static prefix
+    ([FB] Mecanismo Central), so the other rows' cached values are current.
+    Returns bool [B, Nb]."""
+    return updated_positions([q_cur], [q_prev])
+
+
 def head_cosine(q_cur: np.ndarray, q_prev: np.ndarray):
     """Cosine similarity, per (sequence, head), of the head's block Q now vs.
     at the previous step, over all Nb*d values.
@@ -258,9 +304,19 @@ def step_gates(sched):
 
     Returns a list indexed by step t = 1..S (entry 0 unused) of dicts with
     'm' (int32 [B]), 'cos' (float64 [B, Hq] or None), 'decision' (uint8
-    [B, Hq]).  Step 1 has no valid cache and recomputes everything.
+    [B, Hq]).  Step 1 has no valid cache and recomputes everything.  gate
+    "count" counts the positions updated into step t, "count_cum" those
+    updated since the last refresh (cumulative_gates), "cosine" is the
+    per-head similarity gate.
     """
     out = [None]
+    if sched.gate == "count_cum":
+        changed = [None] + [updated_positions([sched.q[t], sched.k[t], sched.v[t]],
+                                              [sched.q[t - 1], sched.k[t - 1], sched.v[t - 1]])
+                            for t in range(1, sched.steps + 1)]
+        for g in cumulative_gates(changed, sched.tau, sched.hq)[1:]:
+            out.append(dict(m=g["m"], cos=None, decision=g["decision"]))
+        return out
     for t in range(1, sched.steps + 1):
         valid = t > 1
         m = update_count([sched.q[t], sched.k[t], sched.v[t]],
@@ -335,13 +391,16 @@ def block_rows(sched, t: int, b: int, h: int, rows=None):
     return attention(q, k, v, sched.scale)
 
 
-def run_block(sched, exact=False):
+def run_block(sched, exact=False, partial=False):
     """The method on a whole block schedule, all rows of all heads.
 
     For each step: gate; for every (b, h) the gate sends to recompute,
     (A_out, L_out) over the prefix with the current Q replaces the cache
     ([FB] Mecanismo Central: the cache holds A_out and L_out from the last
     time they were computed); (A_in, L_in) over the block; A_full = merge.
+    With partial=True the gate is per row instead (partial refresh): at
+    step 1 every row is computed, afterwards exactly the rows whose Q
+    changed from the previous step (rows_changed), in every head.
     Outputs use the library's row-major layout [B*Nb, Hq, d] / [B*Nb, Hq].
     With exact=True also returns the full attention over prefix + block with
     the current Q (for reporting how stale a reused cache is).
@@ -357,9 +416,15 @@ def run_block(sched, exact=False):
         a_in = np.zeros((B, nb, hq, d))
         l_in = np.zeros((B, nb, hq))
         a_ex = np.zeros((B, nb, hq, d)) if exact else None
+        if partial:
+            redo = np.ones((B, nb), dtype=bool) if t == 1 else rows_changed(sched.q[t], sched.q[t - 1])
         for b in range(B):
             for h in range(hq):
-                if dec[b, h] == 0:
+                if partial:
+                    rows = np.flatnonzero(redo[b])
+                    if rows.size:
+                        a_out[b, rows, h], l_out[b, rows, h] = prefix_rows(sched, t, b, h, rows)
+                elif dec[b, h] == 0:
                     a_out[b, :, h], l_out[b, :, h] = prefix_rows(sched, t, b, h)
                 a_in[b, :, h], l_in[b, :, h] = block_rows(sched, t, b, h)
                 if exact:

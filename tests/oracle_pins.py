@@ -324,3 +324,65 @@ def check_pack(varlen_pack):
         back = np.zeros_like(x)
         back[gather] = x[gather]
         assert np.array_equal(back[locked == 0], x[locked == 0]), "gather/scatter round trip"
+
+
+def check_cumulative_gate(cumulative_gates):
+    """Count gate since the last refresh: a hand-worked schedule and
+    invariants against the per-step count and a sticky per-position mark."""
+    # One sequence of 4 positions, tau = 3; positions updated into steps
+    # 1..7: {2}, {0}, {1}, {1}, {2, 3}, {}, {3}.  Step 1 has no cache
+    # (recompute; the count starts again after it); steps 2-4 count {0},
+    # {0,1}, {0,1}: reuse; step 5 counts {0,1,2,3} = 4 >= 3: recompute; step 6
+    # counts nothing, step 7 {3}.  The per-step count (1, 1, 1, 1, 2, 0, 1)
+    # would have reused at every step after the first.
+    sets = [None, {2}, {0}, {1}, {1}, {2, 3}, set(), {3}]
+    changed = [None] + [np.array([[p in s_ for p in range(4)]]) for s_ in sets[1:]]
+    g = cumulative_gates(changed, tau=3, hq=2)
+    assert [int(x["m"][0]) for x in g[1:]] == [1, 1, 2, 2, 4, 0, 1]
+    assert [int(x["decision"][0, 0]) for x in g[1:]] == [0, 1, 1, 1, 0, 1, 1]
+    assert all((x["decision"][:, 0:1] == x["decision"]).all() for x in g[1:])
+    # Random update sets: never below the per-step count, equal to it right
+    # after a refresh; tau = 0 (always recompute) makes the two identical;
+    # with tau above Nb it is the union of every update since step 1; and it
+    # equals a sticky per-position mark cleared on each recompute.
+    r = np.random.default_rng(4)
+    B, nb, S = 3, 10, 12
+    changed = [None] + [r.random((B, nb)) < 0.15 for _ in range(S)]
+    for tau in (0, 2, 4, nb + 1):
+        g = cumulative_gates(changed, tau=tau, hq=1)
+        mark = np.zeros((B, nb), dtype=bool)
+        for t in range(1, S + 1):
+            step = changed[t].sum(axis=1)
+            m = g[t]["m"]
+            assert (m >= step).all()
+            if t == 1 or tau == 0:
+                assert (m == step).all()
+            else:
+                prev_re = g[t - 1]["decision"][:, 0] == 0
+                assert (m[prev_re] == step[prev_re]).all()
+            if tau == nb + 1 and t > 1:
+                union = np.zeros((B, nb), dtype=bool)
+                for s_ in range(2, t + 1):
+                    union |= changed[s_]
+                assert (m == union.sum(axis=1)).all()
+            mark |= changed[t]
+            assert (m == mark.sum(axis=1)).all()
+            assert (g[t]["decision"][:, 0] == ((m < tau) & (t > 1))).all()
+            mark[g[t]["decision"][:, 0] == 0] = False
+
+
+def check_rows_changed(rows_changed):
+    """The rows a partial refresh recomputes: a Q change in any head marks
+    its position, K/V changes do not count, nothing else is marked."""
+    r = np.random.default_rng(6)
+    q0 = r.integers(0, 1 << 16, size=(2, 6, 4, 8), dtype=np.uint16)
+    assert not rows_changed(q0.copy(), q0).any()
+    q = q0.copy()
+    q[1, 4, 3, 7] ^= 1
+    q[0, 0, 0, 0] ^= 0x8000
+    got = rows_changed(q, q0)
+    assert got.shape == (2, 6) and got.sum() == 2 and got[1, 4] and got[0, 0]
+    f = r.standard_normal((1, 3, 2, 4)).astype(np.float32)
+    g = f.copy()
+    g[0, 2, 1, 3] = np.nextafter(g[0, 2, 1, 3], np.float32(np.inf))
+    assert rows_changed(g, f).tolist() == [[False, False, True]]

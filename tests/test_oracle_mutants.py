@@ -138,3 +138,68 @@ def pack_reversed(locked, bs):
 def test_pack_mutants_fail(mutant):
     with pytest.raises(AssertionError):
         pins.check_pack(mutant)
+
+
+# --- cumulative count gate mutants ------------------------------------------
+
+def cum_never_restarts(changed, tau, hq):
+    # counts from step 1 whatever the refreshes
+    out = [None]
+    union = None
+    for t in range(1, len(changed)):
+        union = changed[t].copy() if union is None else union | changed[t]
+        m = union.sum(axis=1).astype(np.int32)
+        out.append(dict(m=m, decision=oracle.gate_count(m, tau, t > 1, hq)))
+    return out
+
+
+def cum_includes_refresh_step(changed, tau, hq):
+    # the union also takes the refresh step's own updates (off by one)
+    out = [None]
+    for t in range(1, len(changed)):
+        B = changed[t].shape[0]
+        m = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            r = 0
+            for s_ in range(1, t):
+                if out[s_]["decision"][b, 0] == 0:
+                    r = s_
+            union = np.zeros(changed[t].shape[1], dtype=bool)
+            for s_ in range(max(r, 1), t + 1):
+                union |= changed[s_][b]
+            m[b] = int(union.sum())
+        out.append(dict(m=m, decision=oracle.gate_count(m, tau, t > 1, hq)))
+    return out
+
+
+def cum_tie_reuses(changed, tau, hq):
+    return oracle.cumulative_gates(changed, tau + 1, hq)   # reuse iff M <= tau
+
+
+def cum_per_step(changed, tau, hq):
+    out = [None]
+    for t in range(1, len(changed)):
+        m = changed[t].sum(axis=1).astype(np.int32)
+        out.append(dict(m=m, decision=oracle.gate_count(m, tau, t > 1, hq)))
+    return out
+
+
+@pytest.mark.parametrize("mutant", [cum_never_restarts, cum_includes_refresh_step, cum_tie_reuses, cum_per_step])
+def test_cumulative_gate_mutants_fail(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_cumulative_gate(mutant)
+
+
+def rows_first_head_only(q_cur, q_prev):
+    return oracle.rows_changed(np.asarray(q_cur)[:, :, :1], np.asarray(q_prev)[:, :, :1])
+
+
+def rows_by_value(q_cur, q_prev):
+    # compares values after a lossy float conversion instead of bits
+    return (np.asarray(q_cur).astype(np.float16) != np.asarray(q_prev).astype(np.float16)).any(axis=(2, 3))
+
+
+@pytest.mark.parametrize("mutant", [rows_first_head_only, rows_by_value])
+def test_rows_changed_mutants_fail(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_rows_changed(mutant)

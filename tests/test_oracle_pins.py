@@ -239,3 +239,32 @@ def test_kl_pins():
     # a lock is sticky, and only eligible tokens lock
     upd = oracle.lock_update([1, 0, 0, 0], [0, 1, 0, 1], np.array([9.0, 0.1, 0.0, 2.0]), 0.5)
     assert upd.tolist() == [1, 1, 0, 0]
+
+
+def test_cumulative_gate_pins():
+    pins.check_cumulative_gate(oracle.cumulative_gates)
+
+
+def test_rows_changed_pins():
+    pins.check_rows_changed(oracle.rows_changed)
+
+
+def test_partial_refresh_is_exact():
+    # A_out/L_out of a row depend on its query only, so refreshing just the
+    # rows whose Q changed keeps the whole cache equal to a full recompute
+    # with the current Q at every step (to rounding of the row subset).
+    s = make_block_schedule(B=2, hq=4, hkv=2, d=16, lp=37, nb=6, steps=5, schedule="redraw",
+                            redraw_range=(1, 2), seed=12)
+    steps = oracle.run_block(s, partial=True)
+    for t in range(1, s.steps + 1):
+        for b in range(s.B):
+            for h in range(s.hq):
+                a, l_ = oracle.prefix_rows(s, t, b, h)
+                np.testing.assert_allclose(steps[t]["a_out"].reshape(s.B, s.nb, s.hq, s.d)[b, :, h], a,
+                                           rtol=0, atol=1e-12)
+                np.testing.assert_allclose(steps[t]["l_out"].reshape(s.B, s.nb, s.hq)[b, :, h], l_,
+                                           rtol=0, atol=1e-12)
+    # with no Q change after step 1 nothing is recomputed
+    n = make_block_schedule(B=1, hq=2, hkv=2, d=16, lp=20, nb=4, steps=3, schedule="none", seed=3)
+    st = oracle.run_block(n, partial=True)
+    assert np.array_equal(st[1]["a_out"], st[3]["a_out"])

@@ -88,7 +88,7 @@ class BlockSchedule:
     nb: int
     steps: int
     scale: float
-    gate: str          # "count" or "cosine"
+    gate: str          # "count", "count_cum" (since the last refresh) or "cosine"
     tau: int
     gamma: float
     seed: int
