@@ -9,6 +9,8 @@ from ._lib import BaError, lib  # noqa: F401
 from .api import (  # noqa: F401
     BA_GATE_COUNT,
     BA_GATE_COSINE,
+    BA_GATE_COUNT_CUM,
+    BA_GATE_ROWS,
     ba_block_attn,
     ba_debug_set_gate_spin_limit,
     ba_gated_split_attn,
@@ -17,6 +19,7 @@ from .api import (  # noqa: F401
     ba_lse_merge,
     ba_prefix_attn,
     ba_prefix_attn_merge,
+    ba_prefix_attn_rows,
     ba_prefix_attn_workspace,
     ba_reuse_gate,
     ba_reuse_gate_workspace,

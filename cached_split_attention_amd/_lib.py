@@ -20,7 +20,7 @@ BA_OK = 0
 STATUS_NAMES = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_DTYPE",
                 4: "BA_ERR_UNSUPPORTED", 5: "BA_ERR_WORKSPACE", 6: "BA_ERR_HIP"}
 BA_BF16, BA_F32 = 0, 1
-BA_GATE_COUNT, BA_GATE_COSINE = 0, 1
+BA_GATE_COUNT, BA_GATE_COSINE, BA_GATE_COUNT_CUM, BA_GATE_ROWS = 0, 1, 2, 3
 
 c_i64x3 = ctypes.c_int64 * 3
 c_i64x2 = ctypes.c_int64 * 2
@@ -47,7 +47,7 @@ class GateDesc(ctypes.Structure):
         ("k_cur", ctypes.c_void_p), ("k_prev", ctypes.c_void_p),
         ("v_cur", ctypes.c_void_p), ("v_prev", ctypes.c_void_p), ("kv_stride", c_i64x3),
         ("upd_mask", ctypes.c_void_p), ("tau", ctypes.c_int32), ("gamma", ctypes.c_double),
-        ("cache_valid", ctypes.c_int32),
+        ("cache_valid", ctypes.c_int32), ("since_refresh", ctypes.c_void_p),
     ]
 
 
@@ -55,6 +55,9 @@ EXPORTS = {
     "ba_prefix_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc)]),
     "ba_prefix_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "ba_prefix_attn_rows": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
     "ba_sparse_prefix_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc), ctypes.c_int32]),
     "ba_sparse_prefix_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,

@@ -13,14 +13,14 @@ import ctypes
 
 import torch
 
-from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_COSINE,
-                   c_i64x2, check, lib)
+from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_COSINE, BA_GATE_COUNT_CUM,
+                   BA_GATE_ROWS, c_i64x2, check, lib)
 
 __all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge", "ba_split_attn",
            "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
            "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
            "ba_debug_set_gate_spin_limit", "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn", "ba_kl_lock",
-           "BA_GATE_COUNT", "BA_GATE_COSINE"]
+           "ba_prefix_attn_rows", "BA_GATE_COUNT", "BA_GATE_COSINE", "BA_GATE_COUNT_CUM", "BA_GATE_ROWS"]
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -145,6 +145,27 @@ def ba_prefix_attn(q, k, v, a_out, l_out, workspace=None, *, q_layout="bshd", kv
                                _stream(stream)))
 
 
+def ba_prefix_attn_rows(q, k, v, cu_rows, rows, a_out, l_out, workspace=None, *, kv_layout="bhsd", scale=None,
+                        stream=None):
+    """Partial refresh: prefix attention for the listed block rows only (q [B, Nb, hq, d] dense;
+    cu_rows int32 [B + 1] and rows int32 (global rows b*Nb + position) as ba_varlen_pack writes
+    them), written into those rows of the cache a_out [B*Nb, hq, d] / l_out [B*Nb, hq].  The
+    workspace is the one ba_prefix_attn_workspace(q, k, v) sizes."""
+    desc, n_rows = _desc(q, k, v, q_layout="bshd", kv_layout=kv_layout, cu_q=None, cu_k=None,
+                         max_q=None, max_k=None, scale=scale, decision=None)
+    _need_gpu(cu_rows, rows, workspace)
+    for t, nm in ((cu_rows, "cu_rows"), (rows, "rows")):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous 1-D int32 tensor")
+    if cu_rows.numel() != desc.n_seq + 1:
+        raise ValueError("cu_rows must have n_seq + 1 entries")
+    _check_out(a_out, (n_rows, desc.hq, desc.d), torch.float32, "a_out")
+    _check_out(l_out, (n_rows, desc.hq), torch.float32, "l_out")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().ba_prefix_attn_rows(ctypes.byref(desc), _ptr(cu_rows), _ptr(rows), _ptr(a_out), _ptr(l_out),
+                                    _ptr(workspace), nbytes, _stream(stream)))
+
+
 def _blocks(blocks, desc):
     _need_gpu(blocks)
     if blocks.dtype != torch.int32 or blocks.dim() != 3 or not blocks.is_contiguous() or \
@@ -241,8 +262,9 @@ def ba_lse_merge(a1, l1, a2, l2, a, l=None, stream=None):
                              _stream(stream)))
 
 
-def _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau, gamma, cache_valid):
-    _need_gpu(q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask)
+def _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau, gamma, cache_valid,
+               since_refresh=None):
+    _need_gpu(q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, since_refresh)
     if q_cur.shape != q_prev.shape or q_cur.stride() != q_prev.stride():
         raise ValueError("q_cur and q_prev must share shape and strides")
     g = GateDesc()
@@ -270,6 +292,9 @@ def _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau,
     g.tau = int(tau)
     g.gamma = float(gamma)
     g.cache_valid = 1 if cache_valid else 0
+    if since_refresh is not None:
+        _check_out(since_refresh, (g.n_seq, g.n_blk), torch.uint8, "since_refresh")
+    g.since_refresh = _ptr(since_refresh)
     return g
 
 
@@ -281,12 +306,15 @@ def ba_reuse_gate_workspace(mode, q_cur, q_prev, **kw) -> int:
 
 def ba_reuse_gate(mode, q_cur, q_prev, *, decision, workspace, k_cur=None, k_prev=None, v_cur=None,
                   v_prev=None, upd_mask=None, tau=0, gamma=0.0, cache_valid=True, m_count=None,
-                  cos=None, stream=None):
-    """Reuse decisions (uint8 [n_seq, hq], 1 = reuse) from the count or cosine gate.
+                  cos=None, since_refresh=None, stream=None):
+    """Reuse decisions (uint8 [n_seq, hq], 1 = reuse) from the count, cosine or cumulative
+    count gate (the latter keeps its state in since_refresh, uint8 [n_seq, n_blk]); in rows mode
+    decision is uint8 [n_seq, n_blk], 1 = the row's cached prefix part is current.
     `workspace` must be zero-filled before its first use (the call leaves it zeroed)."""
-    g = _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau, gamma, cache_valid)
+    g = _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau, gamma, cache_valid,
+                   since_refresh)
     _need_gpu(decision, workspace, m_count, cos)
-    _check_out(decision, (g.n_seq, g.hq), torch.uint8, "decision")
+    _check_out(decision, (g.n_seq, g.n_blk if mode == BA_GATE_ROWS else g.hq), torch.uint8, "decision")
     _check_out(m_count, (g.n_seq,), torch.int32, "m_count")
     _check_out(cos, (g.n_seq, g.hq), torch.float64, "cos")
     nbytes = workspace.numel() * workspace.element_size()
@@ -303,15 +331,16 @@ def ba_gated_split_attn_gate_workspace(mode, q_cur, q_prev, **kw) -> int:
 def ba_gated_split_attn(mode, q_prev, kp, vp, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None,
                         workspace=None, *, q, decision, gate_workspace, k_prev=None, v_prev=None,
                         upd_mask=None, tau=0, gamma=0.0, cache_valid=True, m_count=None, cos=None,
-                        kv_layout="bhsd", scale=None, stream=None):
+                        since_refresh=None, kv_layout="bhsd", scale=None, stream=None):
     """The reuse gate (q/k/v against q_prev/k_prev/v_prev; count or cosine mode) and the
     split attention it gates, as ba_reuse_gate followed by ba_split_attn with
     decision = (decision if cache_valid else None), in two launches.  Dense
     block tensors [B, Nb, H, d]; `gate_workspace` is sized by
     ba_gated_split_attn_gate_workspace and zero-filled before its first use."""
-    count = mode == BA_GATE_COUNT
+    count = mode in (BA_GATE_COUNT, BA_GATE_COUNT_CUM)
     g = _gate_desc(mode, q, q_prev, k if count else None, k_prev if count else None,
-                   v if count else None, v_prev if count else None, upd_mask, tau, gamma, cache_valid)
+                   v if count else None, v_prev if count else None, upd_mask, tau, gamma, cache_valid,
+                   since_refresh)
     _need_gpu(decision, gate_workspace, m_count, cos)
     _check_out(decision, (g.n_seq, g.hq), torch.uint8, "decision")
     _check_out(m_count, (g.n_seq,), torch.int32, "m_count")

@@ -385,8 +385,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[MB], u32x4 (&pk)[MB][2]
 
 // Where one lane's query row lives and what it writes.
 struct RowOut {
-  int64_t orow;    // output row (packed row for varlen, b*max_q + i dense)
-  int64_t prow;    // dense row b*max_q + i (split partials are laid out dense)
+  int64_t orow;    // output row (packed row for varlen, else the dense row)
+  int64_t prow;    // b*max_q + i (split partials are laid out dense, by row index)
   int h;           // query head
   int hf;          // lane half: dims 8j + 4*hf .. +3 of each 32-dim block
   int split;
@@ -516,7 +516,9 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   it.nk = p.max_k;
   if (p.cu_q != nullptr) {
     it.qbase = p.cu_q[it.b];
-    it.nq = p.cu_q[it.b + 1] - it.qbase;
+    it.nq = min(max(p.cu_q[it.b + 1] - it.qbase, 0), p.max_q);   // (rows beyond max_q are ignored)
+  }
+  if (p.cu_k != nullptr) {
     it.kbase = p.cu_k[it.b];
     it.nk = p.cu_k[it.b + 1] - it.kbase;
   }
@@ -573,7 +575,7 @@ __device__ __forceinline__ bool any_recompute(const AttnParams& p, const Item& i
 __device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
   __shared__ int s_r;
   if (threadIdx.x == 0) {
-    const bool count = p.gate_mode == BA_GATE_COUNT;
+    const bool count = p.gate_mode != BA_GATE_COSINE;   // count or cumulative count
     const int32_t* word = p.ready + (int)(blockIdx.x % kReadyCopies) * p.ready_stride + b;
     const int r = gate::wait_ready(word, count ? gate::kCountReady : p.hq, p.spin_limit);
     int res;
@@ -643,7 +645,8 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
     }
   }
   if (gated && !any_recompute<RW * 32>(p, itm)) return;
-  const bool varlen = p.cu_q != nullptr;
+  const bool qvar = p.cu_q != nullptr && p.q_rows == nullptr;   // packed Q rows
+  const bool kvar = p.cu_k != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
   const int R = G * nq;
 
@@ -653,8 +656,9 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   const int g = rvalid ? r / nq : 0;
   const int i = rvalid ? r - g * nq : 0;
   const int h = kvh * G + g;
+  const int qi = (p.q_rows && rvalid) ? listed_row(p, b, itm.qbase + i) : i;   // dense position
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-      (varlen ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
+      (qvar ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)qi * p.qs1) +
       (int64_t)h * p.qs2;
   bf16x8 qf[KS];
 #pragma unroll
@@ -664,9 +668,9 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   }
 
   const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
-      (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
+      (kvar ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
   const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
-      (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
+      (kvar ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
   // key-block list mode: tiles are the listed blocks (KTILE == kBlockKeys)
   const bool listed = p.kblocks != nullptr;
   const int entry = load_block_entry(p, itm, lane);
@@ -684,7 +688,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   float cache_l = 0.0f;
   if constexpr (kPrefetchCache) {
     if (p.mode == kBlock && p.a_cache && rvalid) {
-      const int64_t ce = (varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i) * p.hq + h;
+      const int64_t ce = (qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi) * p.hq + h;
       cache_l = p.l_cache[ce];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -783,7 +787,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
 
   bool writer = kg == 0 && rvalid;
   if (gated) writer = writer && !reused(p, b, h);
-  const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
+  const RowOut ro{qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
 }
@@ -839,7 +843,8 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
     }
   }
   if (gated && !any_recompute<ROWS>(p, itm)) return;
-  const bool varlen = p.cu_q != nullptr;
+  const bool qvar = p.cu_q != nullptr && p.q_rows == nullptr;   // packed Q rows
+  const bool kvar = p.cu_k != nullptr;
   const int G = p.group, nq = itm.nq, b = itm.b, kvh = itm.kvh, kb = itm.kb, ke = itm.ke;
   const int R = G * nq;
 
@@ -849,8 +854,9 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   const int g = rvalid ? r / nq : 0;
   const int i = rvalid ? r - g * nq : 0;
   const int h = kvh * G + g;
+  const int qi = (p.q_rows && rvalid) ? listed_row(p, b, itm.qbase + i) : i;   // dense position
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-      (varlen ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
+      (qvar ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)qi * p.qs1) +
       (int64_t)h * p.qs2;
   bf16x8 qf[KS];
 #pragma unroll
@@ -860,9 +866,9 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   }
 
   const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
-      (varlen ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
+      (kvar ? (int64_t)itm.kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
   const uint16_t* vptr = static_cast<const uint16_t*>(p.v) +
-      (varlen ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
+      (kvar ? (int64_t)itm.kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
   // key-block list mode: tiles are the listed blocks (KT == kBlockKeys)
   const bool listed = p.kblocks != nullptr;
   const int entry = load_block_entry(p, itm, lane);
@@ -927,7 +933,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   const float l_tot = pair_sum(l_run);
   bool writer = rvalid;
   if (gated) writer = writer && !reused(p, b, h);
-  const RowOut ro{varlen ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + i, (int64_t)b * p.max_q + i, h, hf,
+  const RowOut ro{qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
   write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
 }
@@ -961,11 +967,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
   int nq = p.max_q, nk = p.max_k, qbase = 0;
   if (p.cu_q) {
     qbase = p.cu_q[b];
-    nq = p.cu_q[b + 1] - qbase;
-    nk = p.cu_k[b + 1] - p.cu_k[b];
+    nq = min(max(p.cu_q[b + 1] - qbase, 0), p.max_q);
   }
+  if (p.cu_k) nk = p.cu_k[b + 1] - p.cu_k[b];
   if (i >= nq) return;
-  const int64_t oo = (p.cu_q ? (int64_t)(qbase + i) : vrow) * p.hq + h;
+  const int64_t orow = p.q_rows ? (int64_t)b * p.max_q + listed_row(p, b, qbase + i)
+                                : (p.cu_q ? (int64_t)(qbase + i) : vrow);
+  const int64_t oo = orow * p.hq + h;
   // With a decision to read, the loads that do not depend on it (the in-block
   // part and, speculatively, the cached A_out/L_out) go out with it, so a
   // reused entry costs one memory round trip.

@@ -39,25 +39,29 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const AttnParams p) {
   const int64_t vrow = item / p.hq;
   const int b = (int)(vrow / p.max_q);
   const int i = (int)(vrow - (int64_t)b * p.max_q);
-  const bool varlen = p.cu_q != nullptr;
+  const bool qvar = p.cu_q != nullptr && p.q_rows == nullptr;   // packed Q rows
+  const bool kvar = p.cu_k != nullptr;
   int qbase = 0, nq = p.max_q, kbase = 0, nk = p.max_k;
-  if (varlen) {
+  if (p.cu_q) {
     qbase = p.cu_q[b];
-    nq = p.cu_q[b + 1] - qbase;
+    nq = min(max(p.cu_q[b + 1] - qbase, 0), p.max_q);
+  }
+  if (kvar) {
     kbase = p.cu_k[b];
     nk = p.cu_k[b + 1] - kbase;
   }
   if (i >= nq) return;
+  const int qi = p.q_rows ? listed_row(p, b, qbase + i) : i;   // dense position
   if (p.mode != kBlock && p.decision && p.decision[b * p.hq + h]) return;
   const int kvh = h / p.group;
 
   const float* qrow = static_cast<const float*>(p.q) +
-      (varlen ? (int64_t)(qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)i * p.qs1) +
+      (qvar ? (int64_t)(qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)qi * p.qs1) +
       (int64_t)h * p.qs2;
   const float* kptr = static_cast<const float*>(p.k) +
-      (varlen ? (int64_t)kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
+      (kvar ? (int64_t)kbase * p.ks1 : (int64_t)b * p.ks0) + (int64_t)kvh * p.ks2;
   const float* vptr = static_cast<const float*>(p.v) +
-      (varlen ? (int64_t)kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
+      (kvar ? (int64_t)kbase * p.vs1 : (int64_t)b * p.vs0) + (int64_t)kvh * p.vs2;
 
   float q[D];
 #pragma unroll
@@ -112,7 +116,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const AttnParams p) {
   const bool has = l_run > 0.0f;
   const float inv = has ? 1.0f / l_run : 0.0f;
   const float L = has ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  const int64_t orow = varlen ? (int64_t)(qbase + i) : vrow;
+  const int64_t orow = qvar ? (int64_t)(qbase + i) : (int64_t)b * p.max_q + qi;
   const int64_t oe = orow * p.hq + h;
 
   if (p.mode == kPrefixFinal) {

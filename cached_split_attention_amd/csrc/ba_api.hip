@@ -210,7 +210,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
                       const float* l_in, float* a_full, float* l_full, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, ba::AttnParams* block = nullptr,
                       const ba_attn_desc* block_desc = nullptr, const ba::GateParams* gate = nullptr,
-                      const int32_t* kblocks = nullptr, int n_kblocks = -1) {
+                      const int32_t* kblocks = nullptr, int n_kblocks = -1, const int32_t* cu_rows = nullptr,
+                      const int32_t* rows = nullptr) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
@@ -236,6 +237,10 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   p.l = l_out;
   p.kblocks = kblocks;
   p.n_kblocks = kblocks ? n_kblocks : 0;
+  if (rows) {
+    p.cu_q = cu_rows;
+    p.q_rows = rows;
+  }
   if (gate) {
     p.ready = gate->ready;
     p.ready_stride = gate->ready_stride;
@@ -329,6 +334,20 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
                          size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
   return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+ba_status ba_prefix_attn_rows(const ba_attn_desc* desc, const int32_t* cu_rows, const int32_t* rows, float* a_out,
+                              float* l_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  AttnShape sh;
+  const ba_status st = check_desc(desc, &sh);
+  if (st != BA_OK) return st;
+  if (desc->cu_q || desc->cu_k) return fail(BA_ERR_UNSUPPORTED, "row lists are for dense descriptors");
+  if (desc->decision) return fail(BA_ERR_SHAPE, "the descriptor's decision must be NULL (the row list selects)");
+  if (desc->n_seq > 0 && desc->max_q > 0 && (!cu_rows || !rows))
+    return fail(BA_ERR_NULL, "cu_rows and rows are required");
+  return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                     nullptr, nullptr, nullptr, nullptr, -1, cu_rows, rows);
 }
 
 ba_status ba_prefix_attn_merge(const ba_attn_desc* desc, float* a_out, float* l_out, const float* a_in,
@@ -434,14 +453,20 @@ namespace {
 ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint8_t* decision, void* workspace,
                       size_t workspace_bytes, ba::GateParams* out) {
   if (!g) return fail(BA_ERR_NULL, "gate descriptor is NULL");
-  if (g->mode != BA_GATE_COUNT && g->mode != BA_GATE_COSINE) return fail(BA_ERR_SHAPE, "unknown gate mode %d", g->mode);
+  if (g->mode != BA_GATE_COUNT && g->mode != BA_GATE_COSINE && g->mode != BA_GATE_COUNT_CUM &&
+      g->mode != BA_GATE_ROWS)
+    return fail(BA_ERR_SHAPE, "unknown gate mode %d", g->mode);
   if (g->dtype != BA_BF16 && g->dtype != BA_F32) return fail(BA_ERR_DTYPE, "unknown dtype %d", g->dtype);
   if (g->n_seq < 0 || g->n_blk < 1 || g->hq < 1 || g->d < 1)
     return fail(BA_ERR_SHAPE, "sizes n_seq %d, n_blk %d, hq %d, d %d", g->n_seq, g->n_blk, g->hq, g->d);
   if (g->n_seq > 65535 || g->n_blk > 0x7fffffff / 2) return fail(BA_ERR_UNSUPPORTED, "too many sequences");
   if (!decision) return fail(BA_ERR_NULL, "decision is required");
-  const bool count = g->mode == BA_GATE_COUNT;
+  const bool count = g->mode != BA_GATE_COSINE;   // count, cumulative count or rows
   if (count && !m_count) return fail(BA_ERR_NULL, "m_count is required in count mode");
+  if (g->mode == BA_GATE_COUNT_CUM && !g->since_refresh)
+    return fail(BA_ERR_NULL, "since_refresh is required in cumulative count mode");
+  if (g->mode == BA_GATE_ROWS && (g->k_cur || g->k_prev || g->v_cur || g->v_prev))
+    return fail(BA_ERR_SHAPE, "the rows gate reads Q only (k and v must be NULL)");
   if (count && g->n_blk > 65535) return fail(BA_ERR_UNSUPPORTED, "count gate supports n_blk <= 65535");
   if (count && !g->upd_mask) {
     if (!g->q_cur || !g->q_prev) return fail(BA_ERR_NULL, "q_cur and q_prev are required");
@@ -484,6 +509,7 @@ ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint
   p.tau = g->tau;
   p.gamma = g->gamma;
   p.cache_valid = g->cache_valid ? 1 : 0;
+  p.since = g->mode == BA_GATE_COUNT_CUM ? g->since_refresh : nullptr;
   p.chunks = count ? 1 : ba::gate_cos_chunks(g->n_blk, g->d);
   bool v16 = (g->d * p.esize) % 16 == 0;
   const void* ptrs[6] = {g->q_cur, g->q_prev, g->k_cur, g->k_prev, g->v_cur, g->v_prev};
@@ -547,6 +573,8 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
       gate->dtype != prefix->dtype)
     return fail(BA_ERR_SHAPE, "gate and attention descriptors must share n_seq, hq, block size and dtype");
   if (prefix->decision) return fail(BA_ERR_SHAPE, "the prefix descriptor's decision must be NULL (the gate's is used)");
+  if (gate->mode == BA_GATE_ROWS)
+    return fail(BA_ERR_UNSUPPORTED, "the rows gate feeds ba_prefix_attn_rows, not a fused step");
   // The prefix part is gated by this call's decisions only when the cache
   // is valid; otherwise every head recomputes and nothing waits.
   ba_attn_desc pd = *prefix;

@@ -59,8 +59,21 @@ struct AttnParams {
   // chunk and the item key ranges then count list entries, not keys.
   const int32_t* kblocks;
   int n_kblocks;
+  // Row-list mode (dense prefix only, with cu_q set and cu_k NULL): the
+  // query rows of sequence b are list entries j in [cu_q[b], cu_q[b+1]),
+  // entry j naming the dense row q_rows[j] = b * max_q + position; Q is read
+  // and A_out/L_out written at that dense row, other rows stay untouched.
+  const int32_t* q_rows;
 };
 constexpr int kBlockKeys = 64;   // keys per listed key block = the prefix kernels' tile
+
+// Row-list mode: the position named by list entry j of sequence b, clamped
+// into [0, max_q) so that bad device data can give a wrong result but never
+// an access outside Q or the cache.
+__device__ __forceinline__ int listed_row(const AttnParams& p, int b, int j) {
+  const int pos = p.q_rows[j] - b * p.max_q;
+  return min(max(pos, 0), p.max_q - 1);
+}
 
 
 // Launch-shape choice for the bf16 matrix-core kernel.
@@ -115,6 +128,7 @@ struct GateParams {
   double* ws_dbl;      // cosine partials
   int32_t* ready;      // NULL, or the ready words (kReadyCopies copies)
   int ready_stride;    // ints between copies
+  uint8_t* since;      // cumulative count mode: positions updated since the last refresh
 };
 constexpr int kReadyCopies = 4;
 int gate_grid(const GateParams& p);

@@ -32,19 +32,19 @@ int gate_cos_chunks(int n_blk, int d) {
 }
 
 size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d) {
-  if (mode == BA_GATE_COUNT) return (size_t)n_seq * sizeof(int32_t);
+  if (mode != BA_GATE_COSINE) return (size_t)n_seq * sizeof(int32_t);
   const size_t nbh = (size_t)n_seq * hq;
   const size_t ints = (nbh * sizeof(int32_t) + 15) & ~(size_t)15;
   return ints + nbh * gate_cos_chunks(n_blk, d) * 3 * sizeof(double);
 }
 
 int gate_grid(const GateParams& p) {
-  return p.mode == BA_GATE_COUNT ? p.n_blk * p.n_seq : p.chunks * p.hq * p.n_seq;
+  return p.mode != BA_GATE_COSINE ? p.n_blk * p.n_seq : p.chunks * p.hq * p.n_seq;
 }
 
 hipError_t launch_gate(const GateParams& p, hipStream_t s) {
   if (p.n_seq == 0 || p.n_blk == 0) return hipSuccess;
-  if (p.mode == BA_GATE_COUNT) {
+  if (p.mode != BA_GATE_COSINE) {
     dim3 grid(p.n_blk, p.n_seq);
     if (p.vec16)
       hipLaunchKernelGGL(gate_count_kernel<gate::u32x4>, grid, dim3(256), 0, s, p);

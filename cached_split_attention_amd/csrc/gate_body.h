@@ -5,7 +5,13 @@
 //   count  - M_b = number of block positions whose Q, K or V row changed
 //            (bitwise) since the previous step; reuse iff M_b < tau;
 //   cosine - per head, the cosine of the block Q against the previous step's,
-//            accumulated in float64; reuse iff cos > gamma.
+//            accumulated in float64; reuse iff cos > gamma;
+//   cumulative count - as count, over the positions updated at any step since
+//            the sequence's cache was last written (a per-position mark kept
+//            by the caller between steps, cleared when the sequence
+//            recomputes);
+//   rows   - per position: is its Q row unchanged (the partial refresh
+//            recomputes only the rows that changed).
 // Workgroups publish partial results, take a ticket with an integer atomic,
 // and the last workgroup of each sequence (count) or (sequence, head)
 // (cosine) finishes the reduction in a fixed order and resets its ticket, so
@@ -112,13 +118,14 @@ __device__ bool position_changed(const GateParams& p, int b, int pos) {
   return diff;
 }
 
-// Count gate, one workgroup per (block position pos, sequence b).  s_m: one
-// int of LDS.
+// Count gate (and its cumulative and per-row forms), one workgroup per
+// (block position pos, sequence b).  s_m: one int of LDS.
 template <typename W>
 __device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
+  const int64_t pe = (int64_t)b * p.n_blk + pos;
   bool diff = false;
   if (p.upd_mask) {
-    diff = threadIdx.x == 0 && p.upd_mask[(int64_t)b * p.n_blk + pos] != 0;
+    diff = threadIdx.x == 0 && p.upd_mask[pe] != 0;
   } else {
     diff = position_changed<W>(p, b, pos);
   }
@@ -127,6 +134,17 @@ __device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
   // count of changed positions (high 16 bits); the last workgroup of the
   // sequence reads the total from its own return value and resets the word.
   if (threadIdx.x == 0) {
+    if (p.mode == BA_GATE_COUNT_CUM) {
+      // marked if updated at any step since the last refresh (with no
+      // valid cache there is none: old marks do not count); the mark is
+      // stored before the ticket so that a clear by the finishing
+      // workgroup lands after it
+      diff = diff || (p.cache_valid && ld_agent(p.since + pe) != 0);
+      st_agent(p.since + pe, (uint8_t)(diff ? 1 : 0));
+      stores_done();
+    } else if (p.mode == BA_GATE_ROWS) {
+      st_agent(p.decision + pe, (uint8_t)(p.cache_valid && !diff ? 1 : 0));
+    }
     const unsigned old = atomicAdd(reinterpret_cast<unsigned*>(p.ws_int) + b, (diff ? 0x10000u : 0u) + 1u);
     *s_m = -1;
     if ((int)(old & 0xffffu) == p.n_blk - 1) {
@@ -140,9 +158,12 @@ __device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
   }
   __syncthreads();
   const int m = *s_m;
-  if (m < 0) return;
+  if (m < 0 || p.mode == BA_GATE_ROWS) return;
   const uint8_t dec = (p.cache_valid && m < p.tau) ? 1 : 0;
   for (int h = threadIdx.x; h < p.hq; h += blockDim.x) st_agent(p.decision + (int64_t)b * p.hq + h, dec);
+  // the cache of b is rewritten this step: nothing is updated since then
+  if (p.mode == BA_GATE_COUNT_CUM && !dec)
+    for (int q = threadIdx.x; q < p.n_blk; q += blockDim.x) st_agent(p.since + (int64_t)b * p.n_blk + q, (uint8_t)0);
 }
 
 __device__ __forceinline__ float load_elem(const void* base, int64_t idx, int esize) {
@@ -219,11 +240,11 @@ __device__ void cos_body(const GateParams& p, int c, int h, int b, double* red) 
   }
 }
 
-// Gate workgroup wg of a grid of gate_grid(p) workgroups (count: position
-// fastest, then sequence; cosine: chunk, head, sequence); lds is scratch of
+// Gate workgroup wg of a grid of gate_grid(p) workgroups (count modes:
+// position fastest, then sequence; cosine: chunk, head, sequence); lds is scratch of
 // at least 3 * blockDim.x doubles.
 __device__ __forceinline__ void run(const GateParams& p, int wg, void* lds) {
-  if (p.mode == BA_GATE_COUNT) {
+  if (p.mode != BA_GATE_COSINE) {
     const int pos = wg % p.n_blk, b = wg / p.n_blk;
     int* s_m = static_cast<int*>(lds);
     if (p.vec16)

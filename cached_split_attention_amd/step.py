@@ -12,14 +12,26 @@ none), and the pass that combines the prefix's key splits also does the
 merge, so a step is two launches on one stream.  The cache stays valid
 until the next block starts.  This module only orders calls and owns
 buffers; it computes nothing itself.
+
+Gate variants: "count_cum" counts the positions updated since each
+sequence's cache was last written (its marks live in a buffer here);
+"partial" refreshes the cache row by row instead of reusing it: the rows
+whose Q changed are found (ba_reuse_gate, rows mode), listed
+(ba_varlen_pack) and recomputed into the cache (ba_prefix_attn_rows), then
+the in-block part is merged with it (ba_block_attn), so every step's result
+equals a full recompute.
 """
 
 from __future__ import annotations
 
 import torch
 
-from .api import (BA_GATE_COUNT, BA_GATE_COSINE, ba_gated_split_attn, ba_gated_split_attn_gate_workspace,
-                  ba_prefix_attn_workspace)
+from .api import (BA_GATE_COUNT, BA_GATE_COSINE, BA_GATE_COUNT_CUM, BA_GATE_ROWS, ba_block_attn,
+                  ba_gated_split_attn, ba_gated_split_attn_gate_workspace, ba_prefix_attn_rows,
+                  ba_prefix_attn_workspace, ba_reuse_gate, ba_reuse_gate_workspace, ba_varlen_pack)
+
+GATE_MODES = {"count": BA_GATE_COUNT, "cosine": BA_GATE_COSINE, "count_cum": BA_GATE_COUNT_CUM,
+              "partial": BA_GATE_ROWS}
 
 
 class CachedBlockAttention:
@@ -27,8 +39,10 @@ class CachedBlockAttention:
 
     kp, kv: prefix K/V [B, Hkv, Lp, d] ("bhsd") or [B, Lp, Hkv, d] ("bshd").
     Block tensors passed to step() are [B, Nb, H, d].
-    gate: "count" (tau on the number of updated positions) or "cosine"
-    (gamma on the per-head cosine of Q against the previous step's).
+    gate: "count" (tau on the number of updated positions), "count_cum"
+    (tau on the number updated since the cache was last written), "cosine"
+    (gamma on the per-head cosine of Q against the previous step's) or
+    "partial" (recompute exactly the rows whose Q changed).
     """
 
     def __init__(self, kp, vp, *, nb, hq, gate="count", tau=0, gamma=0.0, scale=None,
@@ -37,7 +51,9 @@ class CachedBlockAttention:
         self.kv_layout = kv_layout
         self.B = kp.shape[0]
         self.hq, self.nb, self.d = hq, nb, kp.shape[-1]
-        self.mode = BA_GATE_COUNT if gate == "count" else BA_GATE_COSINE
+        if gate not in GATE_MODES:
+            raise ValueError(f"unknown gate {gate!r}")
+        self.mode = GATE_MODES[gate]
         self.tau, self.gamma, self.scale = tau, gamma, scale
         dev = kp.device
         rows = self.B * nb
@@ -50,6 +66,14 @@ class CachedBlockAttention:
         self.decision = torch.zeros(self.B, hq, device=dev, dtype=torch.uint8)
         self.m_count = torch.zeros(self.B, device=dev, dtype=torch.int32)
         self.cos = torch.zeros(self.B, hq, device=dev, dtype=torch.float64)
+        if self.mode == BA_GATE_COUNT_CUM:
+            self.since_refresh = torch.zeros(self.B, nb, device=dev, dtype=torch.uint8)
+        if self.mode == BA_GATE_ROWS:
+            # per-row "cache is current" marks, then the list of rows to redo
+            self.decision = torch.zeros(self.B, nb, device=dev, dtype=torch.uint8)
+            self.cu_rows = torch.zeros(self.B + 1, device=dev, dtype=torch.int32)
+            self.rows = torch.zeros(max(rows, 1), device=dev, dtype=torch.int32)
+            self.n_rows = torch.zeros(1, device=dev, dtype=torch.int32)
         self.cache_valid = False
         self._ws = None
         self._gws = None
@@ -67,8 +91,11 @@ class CachedBlockAttention:
             n = ba_prefix_attn_workspace(q, self.kp, self.vp, kv_layout=self.kv_layout, scale=self.scale)
             self._ws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
         if self._gws is None:
-            kw = {} if self.mode == BA_GATE_COSINE else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
-            n = ba_gated_split_attn_gate_workspace(self.mode, q, q_prev, **kw)
+            if self.mode == BA_GATE_ROWS:
+                n = ba_reuse_gate_workspace(self.mode, q, q_prev)
+            else:
+                kw = {} if self.mode == BA_GATE_COSINE else dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
+                n = ba_gated_split_attn_gate_workspace(self.mode, q, q_prev, **kw)
             self._gws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
 
     def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None):
@@ -78,16 +105,33 @@ class CachedBlockAttention:
         part is not gated by it: everything recomputes."""
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
         main = stream if stream is not None else torch.cuda.current_stream()
-        count = self.mode == BA_GATE_COUNT
+        if self.mode == BA_GATE_ROWS:
+            self._partial_step(q, k, v, q_prev, main)
+            self.cache_valid = True
+            return self.a_full, self.l_full
+        count = self.mode in (BA_GATE_COUNT, BA_GATE_COUNT_CUM)
         ba_gated_split_attn(self.mode, q_prev, self.kp, self.vp, k, v, self.a_out, self.l_out, self.a_in,
                             self.l_in, self.a_full, self.l_full, self._ws, q=q, decision=self.decision,
                             gate_workspace=self._gws, k_prev=k_prev if count else None,
                             v_prev=v_prev if count else None, tau=self.tau, gamma=self.gamma,
                             cache_valid=self.cache_valid, m_count=self.m_count if count else None,
-                            cos=None if count else self.cos, kv_layout=self.kv_layout, scale=self.scale,
-                            stream=main)
+                            cos=None if count else self.cos,
+                            since_refresh=getattr(self, "since_refresh", None), kv_layout=self.kv_layout,
+                            scale=self.scale, stream=main)
         self.cache_valid = True
         return self.a_full, self.l_full
+
+    def _partial_step(self, q, k, v, q_prev, stream):
+        # rows whose Q is unchanged keep their cached prefix part (all rows
+        # are redone when there is no cache yet)
+        ba_reuse_gate(BA_GATE_ROWS, q, q_prev, decision=self.decision, workspace=self._gws,
+                      cache_valid=self.cache_valid, m_count=self.m_count, stream=stream)
+        ba_varlen_pack([self.nb] * self.B, self.decision.view(-1), self.cu_rows, self.rows[:self.B * self.nb],
+                       self.n_rows, stream=stream)
+        ba_prefix_attn_rows(q, self.kp, self.vp, self.cu_rows, self.rows[:self.B * self.nb], self.a_out,
+                            self.l_out, self._ws, kv_layout=self.kv_layout, scale=self.scale, stream=stream)
+        ba_block_attn(q, k, v, a_cache=self.a_out, l_cache=self.l_out, a_in=self.a_in, l_in=self.l_in,
+                      a_full=self.a_full, l_full=self.l_full, scale=self.scale, stream=stream)
 
     def capture(self, q, k, v, steps, new_block=True, kp=None, vp=None):
         """Capture the given steps of a block's schedule as one HIP graph.

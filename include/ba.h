@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { BA_BF16 = 0, BA_F32 = 1 } ba_dtype;
 
-typedef enum { BA_GATE_COUNT = 0, BA_GATE_COSINE = 1 } ba_gate_mode;
+typedef enum { BA_GATE_COUNT = 0, BA_GATE_COSINE = 1, BA_GATE_COUNT_CUM = 2, BA_GATE_ROWS = 3 } ba_gate_mode;
 
 /*
  * Attention descriptor shared by ba_prefix_attn and ba_block_attn.
@@ -110,6 +110,33 @@ typedef struct ba_attn_desc {
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc);
 ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Partial refresh of the cached out-of-block part (FlashBlock, section 2,
+ * "Estrategias de Reutilizacion Adaptativa": the cache is reused while few
+ * block tokens change; here the rows that did change are recomputed and the
+ * rest kept).  A_out/L_out of a query row depend only on that row's Q and
+ * the static prefix K/V, so recomputing exactly the rows whose Q changed
+ * since the cache was written gives the same cache as recomputing all rows,
+ * at the cost of the changed rows.
+ *   desc: a dense prefix descriptor (cu_q = cu_k = decision = NULL) over the
+ *     whole block Q [n_seq, max_q, hq, d] and the prefix K/V, as for
+ *     ba_prefix_attn.
+ *   cu_rows: device int32[n_seq + 1]; rows: device int32[cu_rows[n_seq]]:
+ *     the rows of sequence b are rows[j] - b * max_q for j in
+ *     [cu_rows[b], cu_rows[b + 1]) (at most max_q of them) -- exactly the
+ *     cu_seqlens_q and gather_idx that ba_varlen_pack writes for n_seq
+ *     branches of max_q positions each, with locked = "row is current"
+ *     (ba_reuse_gate in BA_GATE_ROWS mode writes that mask).  A row index
+ *     out of range is clamped into the sequence (a wrong result, never an
+ *     access outside Q or the cache).
+ *   a_out / l_out: the dense cache [n_seq * max_q, hq, d] / [n_seq * max_q,
+ *     hq]; only the listed rows are written.
+ *   workspace: ba_prefix_attn_workspace(desc) bytes.
+ * Errors as for ba_prefix_attn.
+ */
+ba_status ba_prefix_attn_rows(const ba_attn_desc* desc, const int32_t* cu_rows, const int32_t* rows, float* a_out,
+                              float* l_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Prefix attention over listed key blocks only, for the sparse-attention
@@ -209,6 +236,20 @@ ba_status ba_lse_merge(int64_t rows, int32_t d, const float* a1, const float* l1
  *     n_blk*d values) against the previous step's, accumulated in float64:
  *     cos = dot / (sqrt(|q|^2) * sqrt(|q'|^2)), a zero norm giving cos = 0
  *     and recompute; decision[b, h] = cache_valid && cos > gamma.
+ *   BA_GATE_COUNT_CUM: as BA_GATE_COUNT, but M_b counts the positions
+ *     updated at any step since sequence b's cache was last written (the
+ *     count "since the last refresh", a variant the pages leave open next to
+ *     the per-step count).  since_refresh (device uint8[n_seq, n_blk]) holds
+ *     that set between calls: a position is marked when it changes, and all
+ *     of b's marks are cleared when decision[b, :] = 0 (the cache is
+ *     rewritten this step).  A call with cache_valid == 0 clears every mark,
+ *     so the array needs no initialisation before a block's first step.
+ *   BA_GATE_ROWS: per block position (partial refresh, see
+ *     ba_prefix_attn_rows): decision is uint8[n_seq, n_blk] with
+ *     decision[b, p] = cache_valid && position p's Q row (every head) is
+ *     bitwise unchanged (or upd_mask[b, p] == 0); m_count[b] = the number
+ *     of changed positions.  Only Q is read (k_* and v_* must be NULL);
+ *     tau is not used.
  *   Ties (M == tau, cos == gamma) recompute; cache_valid == 0 recomputes all.
  */
 typedef struct ba_gate_desc {
@@ -223,6 +264,7 @@ typedef struct ba_gate_desc {
   int32_t tau;
   double gamma;
   int32_t cache_valid;      /* 0 = no cache yet (first step of a block)        */
+  uint8_t* since_refresh;   /* BA_GATE_COUNT_CUM state; NULL in other modes    */
 } ba_gate_desc;
 
 /*

@@ -165,6 +165,136 @@ def test_gate_cosine_exact_tie_and_zero_norm():
 
 
 # ----------------------------------------------------------------------------
+# gate variants: count since the last refresh, per-row partial refresh
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("use_mask", [False, True])
+def test_gate_count_cumulative(use_mask):
+    # M since the last refresh, the decision and the kept marks at every step
+    # of a schedule whose per-step counts stay below tau while the
+    # cumulative ones cross it now and then.
+    s = make_block_schedule(dtype="bf16", B=3, hq=4, hkv=2, d=64, lp=8, nb=16, steps=14,
+                            schedule="redraw", redraw_range=(0, 2), gate="count_cum", tau=4, seed=53)
+    q = [dev_in(x, s.dtype) for x in s.q]
+    k = [dev_in(x, s.dtype) for x in s.k]
+    v = [dev_in(x, s.dtype) for x in s.v]
+    ref = oracle.step_gates(s)
+    ws = torch.zeros(ba.ba_reuse_gate_workspace(ba.BA_GATE_COUNT_CUM, q[1], q[0], k_cur=k[1], k_prev=k[0],
+                                                v_cur=v[1], v_prev=v[0]), device=DEV, dtype=torch.uint8)
+    dec = torch.empty(s.B, s.hq, device=DEV, dtype=torch.uint8)
+    m = torch.empty(s.B, device=DEV, dtype=torch.int32)
+    since = torch.full((s.B, s.nb), 5, device=DEV, dtype=torch.uint8)   # stale: the first step clears it
+    saw = set()
+    for t in range(1, s.steps + 1):
+        if use_mask:
+            mask = torch.from_numpy(oracle.updated_positions([s.q[t], s.k[t], s.v[t]],
+                                                             [s.q[t - 1], s.k[t - 1], s.v[t - 1]])
+                                    .astype(np.uint8)).to(DEV)
+            ba.ba_reuse_gate(ba.BA_GATE_COUNT_CUM, q[t], q[t - 1], upd_mask=mask, tau=s.tau, cache_valid=t > 1,
+                             m_count=m, decision=dec, workspace=ws, since_refresh=since)
+        else:
+            ba.ba_reuse_gate(ba.BA_GATE_COUNT_CUM, q[t], q[t - 1], k_cur=k[t], k_prev=k[t - 1], v_cur=v[t],
+                             v_prev=v[t - 1], tau=s.tau, cache_valid=t > 1, m_count=m, decision=dec,
+                             workspace=ws, since_refresh=since)
+        torch.cuda.synchronize()
+        got_m, got_d = m.cpu().numpy(), dec.cpu().numpy()
+        assert np.array_equal(got_m, ref[t]["m"]), (t, got_m, ref[t]["m"])
+        assert np.array_equal(got_d, ref[t]["decision"]), t
+        kept = since.cpu().numpy()
+        assert set(np.unique(kept).tolist()) <= {0, 1}
+        # marks: the count's positions while reusing, none after a recompute
+        assert np.array_equal(kept.sum(axis=1), np.where(got_d[:, 0] == 1, got_m, 0)), t
+        assert not ws.any()
+        if t > 1:
+            saw |= set(got_d[:, 0].tolist())
+        assert (got_m >= s.touched[t]).all()
+    assert saw == {0, 1}, "schedule should exercise both decisions"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_rows(dtype):
+    # Rows mode: per position, is its Q row unchanged; K/V are not looked at.
+    s = make_block_schedule(dtype=dtype, B=2, hq=3, hkv=3, d=64, lp=8, nb=40, steps=5, schedule="redraw",
+                            redraw_range=(0, 6), seed=54)
+    q = [dev_in(x, dtype) for x in s.q]
+    ws = torch.zeros(ba.ba_reuse_gate_workspace(ba.BA_GATE_ROWS, q[1], q[0]), device=DEV, dtype=torch.uint8)
+    keep = torch.empty(s.B, s.nb, device=DEV, dtype=torch.uint8)
+    m = torch.empty(s.B, device=DEV, dtype=torch.int32)
+    for t in range(1, s.steps + 1):
+        ba.ba_reuse_gate(ba.BA_GATE_ROWS, q[t], q[t - 1], cache_valid=t > 1, m_count=m, decision=keep,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        ch = oracle.rows_changed(s.q[t], s.q[t - 1])
+        assert np.array_equal(keep.cpu().numpy(), ((~ch) & (t > 1)).astype(np.uint8)), t
+        assert np.array_equal(m.cpu().numpy(), ch.sum(axis=1)), t
+        assert not ws.any()
+    k = dev_in(s.k[1], dtype)
+    with pytest.raises(ba.BaError):
+        ba.ba_reuse_gate(ba.BA_GATE_ROWS, q[1], q[0], k_cur=k, k_prev=k, v_cur=k, v_prev=k, m_count=m,
+                         decision=keep, workspace=ws)
+
+
+ROWS_SHAPES = [
+    # (B, hq, hkv, d, lp, nb): few rows per KV head with split-KV, GQA
+    # 128-row tiles, the alternating kernel, head dim 64, one split
+    (3, 8, 8, 128, 1500, 32),
+    (2, 8, 2, 128, 2000, 64),
+    (1, 4, 1, 128, 900, 80),
+    (2, 6, 3, 64, 555, 41),
+    (2, 4, 4, 128, 64, 24),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", ROWS_SHAPES)
+def test_prefix_attn_rows(dtype, shape):
+    # Listed rows recomputed into the cache; the others untouched.  Sequence
+    # 0 lists a random subset, sequence 1 none (or all rows when it is the
+    # last), the rest random; lists come from ba_varlen_pack.
+    B, hq, hkv, d, lp, nb = shape
+    if dtype == "f32" and lp > 1000:
+        lp = 700
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=lp + nb)
+    want_a, want_l = _oracle_prefix(s)
+    r = np.random.default_rng(nb)
+    sel = r.random((B, nb)) < 0.3
+    if B > 1:
+        sel[1] = B == 2
+    q, kp, vp = dev_in(s.q[0], dtype), dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    keep = torch.from_numpy((~sel).astype(np.uint8).ravel()).to(DEV)
+    cu = torch.empty(B + 1, device=DEV, dtype=torch.int32)
+    rows = torch.empty(B * nb, device=DEV, dtype=torch.int32)
+    total = torch.empty(1, device=DEV, dtype=torch.int32)
+    ba.ba_varlen_pack([nb] * B, keep, cu, rows, total)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    a = torch.full((B * nb, hq, d), 777.0, device=DEV)
+    l = torch.full((B * nb, hq), 777.0, device=DEV)
+    ba.ba_prefix_attn_rows(q, kp, vp, cu, rows, a, l, ws)
+    torch.cuda.synchronize()
+    assert int(total.item()) == int(sel.sum())
+    flat = sel.ravel()
+    ga, gl = host(a), host(l)
+    check_a(ga[flat], want_a[flat], "A_out listed rows")
+    check_l(gl[flat], want_l[flat], "L_out listed rows")
+    assert (ga[~flat] == 777.0).all() and (gl[~flat] == 777.0).all(), "unlisted rows must stay untouched"
+    # a hand-made list in another order, with a repeated row, gives the same
+    # values for the rows it names
+    order = [int(x) for x in np.flatnonzero(flat)[::-1]]
+    if order:
+        order.append(order[0])
+        seq = np.array(order) // nb
+        idx = np.argsort(seq, kind="stable")
+        lst = np.array(order)[idx].astype(np.int32)
+        cu2 = np.searchsorted(seq[idx], np.arange(B + 1)).astype(np.int32)
+        a2 = torch.full_like(a, 777.0)
+        l2 = torch.full_like(l, 777.0)
+        ba.ba_prefix_attn_rows(q, kp, vp, torch.from_numpy(cu2).to(DEV), torch.from_numpy(lst).to(DEV), a2, l2, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(a2)[flat], ga[flat])
+        np.testing.assert_array_equal(host(l2)[flat], gl[flat])
+
+
+# ----------------------------------------------------------------------------
 # ba_varlen_pack
 # ----------------------------------------------------------------------------
 

@@ -83,7 +83,7 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
         torch.cuda.synchronize()
         dec = attn.decision.cpu().numpy()
         assert np.array_equal(dec, gates[t]["decision"]), f"[{name}] step {t}: decisions differ"
-        if sched.gate == "count":
+        if sched.gate in ("count", "count_cum"):
             assert np.array_equal(attn.m_count.cpu().numpy(), gates[t]["m"]), f"[{name}] step {t}: M differs"
         recomputes += int((dec == 0).sum())
         ga, gl = host(af), host(lf)
@@ -129,6 +129,65 @@ def test_workload_long_prefix():
     # prefix, four steps (many key splits per head, and their combine).
     sched, rec = _run_schedule_checked("c2_llada", rows_per_step=3, seed=6, lp=262144, steps=4)
     assert rec >= sched.B * sched.hq
+
+
+def test_workload_gqa_cumulative_gate():
+    # The GQA long-context schedule (Poisson(3) rewritten rows per step, tau
+    # 8) gated on the positions updated since the last refresh: the
+    # per-step count rarely reaches tau, the cumulative one every few steps.
+    sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=4, seed=7, gate="count_cum", steps=16)
+    per_step = oracle.step_gates(preset("c3_gqa_long", steps=16))
+    rec_step = sum(int((per_step[t]["decision"] == 0).sum()) for t in range(1, 17))
+    assert rec > rec_step, (rec, rec_step)
+
+
+def test_workload_llada_cosine_gate():
+    # The per-head similarity gate on the LLaDA-like unmasking schedule (the
+    # dLLM setting rather than video): decisions per (sequence, head).
+    sched, rec = _run_schedule_checked("c2_llada", full_rows=True, gate="cosine", gamma=0.95, steps=16)
+    assert sched.B * sched.hq < rec < sched.steps * sched.B * sched.hq
+
+
+def test_workload_gqa_partial_refresh():
+    # Partial refresh on the GQA long-context schedule: only rows whose Q
+    # changed are recomputed, so every step's A_full equals attention over
+    # prefix + block with the current Q (checked on sampled rows), and the
+    # per-row marks equal the oracle's changed rows.
+    sched = preset("c3_gqa_long", steps=8)
+    say(f"[c3 partial] B={sched.B} Hq={sched.hq} Hkv={sched.hkv} Lp={sched.lp} Nb={sched.nb} steps={sched.steps}")
+    q, k, v = _to_dev(sched)
+    kp, vp = dev_in(sched.kp, sched.dtype), dev_in(sched.vp, sched.dtype)
+    attn = ba.CachedBlockAttention(kp, vp, nb=sched.nb, hq=sched.hq, gate="partial", scale=sched.scale)
+    rng = np.random.default_rng(8)
+    g = sched.hq // sched.hkv
+    redone = 0
+    for t in range(1, sched.steps + 1):
+        af, lf = attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+        torch.cuda.synchronize()
+        ch = oracle.rows_changed(sched.q[t], sched.q[t - 1])
+        want_keep = ((~ch) & (t > 1)).astype(np.uint8)
+        assert np.array_equal(attn.decision.cpu().numpy(), want_keep), f"step {t}: row marks differ"
+        redone += int((want_keep == 0).sum())
+        ga = host(af).reshape(-1, sched.hq, sched.d)
+        gl = host(lf).reshape(-1, sched.hq)
+        picks = [(int(rng.integers(sched.B)), int(rng.integers(sched.hq)), int(rng.integers(sched.nb)))
+                 for _ in range(5)]
+        # a changed row when there is one
+        bs, ps = np.nonzero(ch)
+        if t > 1 and bs.size:
+            picks.append((int(bs[0]), int(rng.integers(sched.hq)), int(ps[0])))
+        for b, h, i in picks:
+            qq = oracle.to_f64(sched.q[t][b, i:i + 1, h, :], sched.dtype)
+            kk = np.concatenate([oracle.to_f64(sched.kp[b, h // g], sched.dtype),
+                                 oracle.to_f64(sched.k[t][b, :, h // g], sched.dtype)])
+            vv = np.concatenate([oracle.to_f64(sched.vp[b, h // g], sched.dtype),
+                                 oracle.to_f64(sched.v[t][b, :, h // g], sched.dtype)])
+            wa, wl = oracle.attention(qq, kk, vv, sched.scale)
+            r = b * sched.nb + i
+            check_a(ga[r, h][None], wa, f"A_full step {t} (b{b} h{h} i{i})")
+            check_l(gl[r, h][None], wl, f"L_full step {t} (b{b} h{h} i{i})")
+    say(f"[c3 partial] {sched.steps} steps checked, {redone} rows recomputed of {sched.steps * sched.B * sched.nb}")
+    assert sched.B * sched.nb < redone < sched.steps * sched.B * sched.nb
 
 
 def test_workload_varlen_branches():
