@@ -47,18 +47,26 @@ KL_SOURCES = ["cached_split_attention_amd/csrc/kl.hip"]
 
 def step_work(s, dec, esize=2):
     """Algorithmic (bytes, flops, prefix_bytes, prefix_flops) of one
-    denoising step of schedule s with decision matrix dec [B, Hq] (1 = reuse).
-    Prefix: K/V of every KV head with a recomputed query head, the Q rows of
-    recomputed heads, A_out/L_out written.  Every step: gate inputs, block Q,
-    K, V, the cache read by the merge, A_full/L_full written."""
+    denoising step of schedule s with decision matrix dec [B, Hq] (1 = reuse),
+    or, for the partial refresh, per-row marks dec [B, Nb] (1 = row current).
+    Prefix: K/V of every KV head with a recomputed query head (partial: of
+    every sequence with a recomputed row), the recomputed Q rows, their
+    A_out/L_out written.  Every step: gate inputs, block Q, K, V, the cache
+    read by the merge, A_full/L_full written."""
     B, hq, hkv, d, lp, nb = s.B, s.hq, s.hkv, s.d, s.lp, s.nb
     g = hq // hkv
     rec = (dec == 0)
-    n_rec = int(rec.sum())
-    kv_heads = int(rec.reshape(B, hkv, g).any(axis=2).sum())
-    p_bytes = kv_heads * lp * d * esize * 2 + n_rec * nb * d * esize + n_rec * nb * (d + 1) * 4
-    p_flops = 4 * d * nb * lp * n_rec
-    if s.gate == "count":
+    if s.gate == "partial":
+        n_rows = int(rec.sum())
+        seqs = int(rec.any(axis=1).sum())
+        p_bytes = seqs * hkv * lp * d * esize * 2 + n_rows * hq * d * esize + n_rows * hq * (d + 1) * 4
+        p_flops = 4 * d * lp * n_rows * hq
+    else:
+        n_rec = int(rec.sum())
+        kv_heads = int(rec.reshape(B, hkv, g).any(axis=2).sum())
+        p_bytes = kv_heads * lp * d * esize * 2 + n_rec * nb * d * esize + n_rec * nb * (d + 1) * 4
+        p_flops = 4 * d * nb * lp * n_rec
+    if s.gate in ("count", "count_cum"):
         gate_bytes = 2 * B * nb * (hq + 2 * hkv) * d * esize
     else:
         gate_bytes = 2 * B * nb * hq * d * esize
@@ -585,6 +593,9 @@ def main():
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated prefix copies")
     ap.add_argument("--lp", type=int, default=None,
                     help="prefix length override for the dense shapes (long-context sweep)")
+    ap.add_argument("--gate", choices=["count", "count_cum", "cosine", "partial"], default=None,
+                    help="gate override for the block schedule (count since the last refresh, per-head "
+                         "cosine, or per-row partial refresh)")
     ap.add_argument("--sparse", type=float, default=None,
                     help="key-block density: time sparse-attention residual reuse instead of the block schedule")
     ap.add_argument("--probe", action="store_true",
@@ -614,7 +625,10 @@ def main():
     def progress(msg):
         print(f"[bench {args.workload}] {msg}", file=sys.stderr, flush=True)
 
-    s = preset(args.workload) if args.lp is None else preset(args.workload, lp=args.lp)
+    over = {} if args.lp is None else dict(lp=args.lp)
+    if args.gate is not None:
+        over["gate"] = args.gate
+    s = preset(args.workload, **over)
     progress(f"inputs drawn (prefix {s.lp})")
 
     def to_dev(x):
