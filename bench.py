@@ -133,7 +133,21 @@ def measured_traffic(workload, name=None, sources=KERNEL_SOURCES):
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(s, budget_s=20.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(s, budget_s=20.0, got=None):
+    """The oracle on whole block schedules of the workload (timed), and, when
+    the GPU's final-step A_full/L_full are given, the errors the GPU path
+    achieves against the oracle's final step."""
     import numpy as np
     import oracle
     try:
@@ -152,10 +166,20 @@ def cpu_baseline(s, budget_s=20.0):
         if time.perf_counter() - t0 >= budget_s / 2 or runs >= 50:
             break
     dt = time.perf_counter() - t0
-    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} full block schedule(s) of the same workload ({s.steps} steps each), "
-                      f"NumPy float64, {dt:.1f} s",
-            "ms_per_step": dt / runs * 1e3}
+    out = {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{runs} full block schedule(s) of the same workload ({s.steps} steps each), "
+                     f"NumPy float64, {dt:.1f} s",
+           "ms_per_step": dt / runs * 1e3, "cpu_model": cpu_model()}
+    if got is not None:
+        ga, gl = got
+        wa, wl = ref[s.steps]["a_full"], ref[s.steps]["l_full"]
+        out["achieved_error"] = {
+            "step": s.steps, "rows": int(wa.shape[0] * wa.shape[1]),
+            "a_full_max_abs": float(np.abs(ga - wa).max()),
+            "a_full_rel_l2": float(np.linalg.norm(ga - wa) / np.linalg.norm(wa)),
+            "l_full_max_abs": float(np.abs(gl - wl).max()),
+            "bars": {"a_max_abs": 2e-2, "a_rel_l2": 5e-3, "l_max_abs": 1e-4}}
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -163,6 +187,46 @@ def cpu_baseline(s, budget_s=20.0):
 # ----------------------------------------------------------------------------
 
 COPY_PROBE_BYTES = 256 << 20
+
+
+def measured_peaks(dev):
+    """Peaks measured on this machine, outside any timed region: a device copy of
+    1 GiB (bytes read + written per second) and a 8192^3 bf16 GEMM
+    (torch.matmul, i.e. the vendor BLAS)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n = (1 << 30) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 5 * n * 4 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        c = torch.matmul(a, b)
+    ev[1].record()
+    torch.cuda.synchronize()
+    gemm_tf = 5 * 2 * m ** 3 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    del a, b, c
+    return {"copy_gbs": round(copy_gbs, 1), "gemm_bf16_tflops": round(gemm_tf, 1)}
+
+
+def with_measured(roof, peaks):
+    """The roofline block plus the achieved rate as a fraction of the
+    matching measured peak."""
+    ref = peaks["copy_gbs"] if roof["bound"] == "hbm" else peaks["gemm_bf16_tflops"]
+    return {**roof, "measured_peak": peaks, "frac_of_measured": round(roof["achieved"] / ref, 4)}
 
 
 def probe(args, s, q, kps, vps):
@@ -302,6 +366,7 @@ def run_varlen(args):
 
     s_bytes, s_flops, p_bytes, p_flops = varlen_work(vb, n_total)
     roof, achieved, achieved_tf = roofline_of(p_bytes, p_flops, pref_us)
+    roof = with_measured(roof, measured_peaks(dev))
     out = {
         "metric": METRIC,
         "value": round(s_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -551,6 +616,7 @@ def run_kl(args):
     us = e0.elapsed_time(e1) * 1e3 / (args.steps * n_copies)
     nbytes = pair_bytes + KL_ROWS * (4 + 1 + 1)
     roof, achieved, _ = roofline_of(nbytes, 1, us)
+    roof = with_measured(roof, measured_peaks(dev))
     out = {
         "metric": METRIC, "value": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": 1, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True,
@@ -658,6 +724,7 @@ def main():
     for t in range(1, s.steps + 1):
         attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
         decisions.append(attn.decision.cpu().numpy().copy())
+    final_out = (attn.a_full.cpu().double().numpy().copy(), attn.l_full.cpu().double().numpy().copy())
     work = [step_work(s, decisions[t]) for t in range(1, s.steps + 1)]
     blk_bytes = sum(w[0] for w in work)
     blk_flops = sum(w[1] for w in work)
@@ -716,6 +783,7 @@ def main():
     p_bytes1, p_flops1 = work[0][2], work[0][3]
     traffic = measured_traffic(args.workload)
     roof, achieved, achieved_tf = roofline_of(p_bytes1, p_flops1, pref_mean_us)
+    roof = with_measured(roof, measured_peaks(dev))
 
     out = {
         "metric": METRIC,
@@ -756,7 +824,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(s)
+        out["cpu_baseline"] = cpu_baseline(s, got=final_out if s.gate != "partial" else None)
     print(json.dumps(out), flush=True)
 
 
