@@ -250,3 +250,33 @@ def test_workload_varlen_branches():
         for nm in ("l_out", "l_in", "l_full"):
             check_l(host(outs[nm])[:tot, h], ref[nm][:, h], f"[c5_varlen split] {nm} head {h}")
     say(f"[c5_varlen] split attention checked on heads {heads}")
+
+
+@pytest.mark.parametrize("gate", ["count_cum", "partial"])
+def test_block_graph_replays_gate_variants(gate):
+    # A whole block captured as one HIP graph under the gate variants and
+    # replayed three times, with unrelated eager work and synchronisation in
+    # between: every replay gives the eager run's final A_full/L_full and
+    # decisions bit for bit (the variants' state -- the since-refresh marks,
+    # the row lists -- is rebuilt by the graph itself).
+    sched = preset("c2_llada", steps=8, gate="count" if gate == "partial" else gate, tau=3)
+    q, k, v = _to_dev(sched)
+    kp, vp = dev_in(sched.kp, sched.dtype), dev_in(sched.vp, sched.dtype)
+    attn = ba.CachedBlockAttention(kp, vp, nb=sched.nb, hq=sched.hq, gate=gate, tau=sched.tau, scale=sched.scale)
+    attn.start_block()
+    for t in range(1, sched.steps + 1):
+        attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+    torch.cuda.synchronize()
+    want = (host(attn.a_full), host(attn.l_full), attn.decision.cpu().numpy().copy())
+    g = attn.capture_block(q, k, v)
+    noise = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        attn.a_full.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(attn.a_full), want[0], err_msg=f"{gate} replay {rep}")
+        np.testing.assert_array_equal(host(attn.l_full), want[1], err_msg=f"{gate} replay {rep}")
+        assert np.array_equal(attn.decision.cpu().numpy(), want[2]), f"{gate} replay {rep}"
+        noise.mul_(1.0001).add_(float(noise.sum().item()) * 0.0)
+    say(f"[graph {gate}] 3 replays match the eager block")
