@@ -164,6 +164,55 @@ def test_gate_cosine_exact_tie_and_zero_norm():
         assert not dec.cpu().numpy().any()
 
 
+def _random_split_shapes(n, seed):
+    # (dtype, B, hq, hkv, d, lp, nb): batch 1-3, GQA group 1-4, head dim 64
+    # or 128, prefixes from empty through ragged multi-split lengths, blocks
+    # from one row to 300, so that every launch shape (few rows, 128-row and
+    # 256-row tiles) and ragged tails come up.
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(r.choice([1, 2, 4]))
+        g = int(r.integers(1, 5))
+        lp = 0 if i % 5 == 4 else int(r.integers(1, 2600))
+        nb = int(r.choice([1, int(r.integers(2, 40)), int(r.integers(40, 120)), int(r.integers(120, 301))]))
+        dt = "f32" if i % 6 == 5 else "bf16"
+        out.append((dt, int(r.integers(1, 4)), hkv * g, hkv, int(r.choice([64, 128])), lp, nb))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_split_shapes(12, 2024))
+def test_split_attn_random_shapes(case):
+    # Seeded random shapes through the one-launch split attention, every head
+    # recomputing: A_out, A_in and A_full against the oracle on all rows.
+    dtype, B, hq, hkv, d, lp, nb = case
+    print(f"case {case}", flush=True)
+    s = _dense_inputs(dtype, B, hq, hkv, d, lp, nb, seed=B * 1000 + lp + nb)
+    rows = B * nb
+    if lp > 0:
+        want_a, want_l = _oracle_prefix(s)
+    else:
+        want_a, want_l = np.zeros((rows, hq, d)), np.full((rows, hq), -np.inf)
+    want_ai, want_li = _oracle_block(s)
+    want_f, want_lf = oracle.merge(want_a, want_l, want_ai, want_li)
+    q, k, v = dev_in(s.q[0], dtype), dev_in(s.k[0], dtype), dev_in(s.v[0], dtype)
+    if lp > 0:
+        kp, vp = dev_in(s.kp, dtype), dev_in(s.vp, dtype)
+    else:
+        kp = vp = torch.zeros(B, hkv, 0, d, device=DEV, dtype=q.dtype)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp, vp)), device=DEV, dtype=torch.uint8)
+    outs = [torch.full((rows, hq, d), 9.0, device=DEV) for _ in range(3)]
+    ls = [torch.full((rows, hq), 9.0, device=DEV) for _ in range(3)]
+    ba.ba_split_attn(q, kp, vp, k, v, outs[0], ls[0], outs[1], ls[1], outs[2], ls[2], ws)
+    torch.cuda.synchronize()
+    check_a(host(outs[0]), want_a, "A_out")
+    check_l(host(ls[0]), want_l, "L_out")
+    check_a(host(outs[1]), want_ai, "A_in")
+    check_l(host(ls[1]), want_li, "L_in")
+    check_a(host(outs[2]), want_f, "A_full")
+    check_l(host(ls[2]), want_lf, "L_full")
+
+
 # ----------------------------------------------------------------------------
 # gate variants: count since the last refresh, per-row partial refresh
 # ----------------------------------------------------------------------------
