@@ -161,3 +161,79 @@ def test_pack_validation(lib):
     assert lib.ba_varlen_pack(600, sizes, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None, None, None, None) == 2
     assert lib.ba_varlen_pack(1, sizes, None, FAKE, FAKE, FAKE, 0, 0, 0, None, None, None, None) == 1
     assert lib.ba_varlen_pack(1, sizes, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, FAKE, None, None, None) == 1
+
+
+def test_rows_validation(lib):
+    # partial refresh: dense descriptors only, no decision, both lists given
+    d = good_desc()
+    st, msg = status_of(lib, lib.ba_prefix_attn_rows, ctypes.byref(d), None, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 1 and "cu_rows" in msg
+    d.decision = FAKE
+    st, msg = status_of(lib, lib.ba_prefix_attn_rows, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 2 and "decision" in msg
+    d = good_desc()
+    d.cu_q = d.cu_k = FAKE
+    st, msg = status_of(lib, lib.ba_prefix_attn_rows, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 4 and "dense" in msg
+    d = good_desc()
+    need = lib.ba_prefix_attn_workspace(ctypes.byref(d))
+    st, msg = status_of(lib, lib.ba_prefix_attn_rows, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == 5 and "workspace" in msg
+    d.n_seq = 0
+    assert lib.ba_prefix_attn_rows(ctypes.byref(d), None, None, FAKE, FAKE, None, 0, None) == 0
+
+
+def test_gate_variant_validation(lib):
+    g = good_gate()
+    g.mode = 2   # count since the last refresh: needs its marks
+    need = lib.ba_reuse_gate_workspace(ctypes.byref(g))
+    assert need == 2 * 4
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, FAKE, FAKE, need, None)
+    assert st == 1 and "since_refresh" in msg
+    g = good_gate()
+    g.mode = 3   # rows: Q only
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), FAKE, None, FAKE, FAKE, need, None)
+    assert st == 2 and "Q only" in msg
+    g.k_cur = g.k_prev = g.v_cur = g.v_prev = None
+    st, msg = status_of(lib, lib.ba_reuse_gate, ctypes.byref(g), None, None, FAKE, FAKE, need, None)
+    assert st == 1 and "m_count" in msg
+    # the rows gate feeds the partial refresh, not the fused step
+    d = good_desc()
+    gws = lib.ba_gated_split_attn_gate_workspace(ctypes.byref(g))
+    g.n_seq, g.hq, g.n_blk = d.n_seq, d.hq, d.max_q
+    st, msg = status_of(lib, lib.ba_gated_split_attn, ctypes.byref(g), FAKE, None, FAKE, FAKE, gws,
+                        ctypes.byref(d), ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == 4 and "rows gate" in msg
+
+
+def test_kl_validation(lib):
+    kl = lib.ba_kl_lock
+    assert kl(-1, 100, 0, FAKE, FAKE, 100, None, 1e-3, FAKE, None, None) == 2
+    assert kl(4, 0, 0, FAKE, FAKE, 100, None, 1e-3, FAKE, None, None) == 2
+    assert kl(4, 100, 9, FAKE, FAKE, 100, None, 1e-3, FAKE, None, None) == 3
+    st, msg = status_of(lib, kl, 4, 100, 0, FAKE, FAKE, 99, None, 1e-3, FAKE, None, None)
+    assert st == 2 and "row_stride" in msg
+    st, msg = status_of(lib, kl, 4, 100, 0, FAKE, FAKE, 100, None, 1e-3, None, None, None)
+    assert st == 1 and "no output" in msg
+    st, msg = status_of(lib, kl, 4, 100, 0, None, FAKE, 100, None, 1e-3, FAKE, None, None)
+    assert st == 1 and "logits" in msg
+    st, msg = status_of(lib, kl, 4, 100, 0, FAKE, FAKE, 100, None, -1.0, FAKE, None, None)
+    assert st == 2 and "eps" in msg
+    assert kl(0, 100, 0, None, None, 100, None, 1e-3, FAKE, None, None) == 0
+
+
+def test_sparse_validation(lib):
+    d = good_desc()
+    n_max = (d.max_k + 63) // 64
+    fn = lib.ba_sparse_prefix_attn
+    st, msg = status_of(lib, fn, ctypes.byref(d), FAKE, n_max + 1, FAKE, FAKE, None, 0, None)
+    assert st == 2 and "n_blocks" in msg
+    st, msg = status_of(lib, fn, ctypes.byref(d), None, 3, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 1 and "blocks" in msg
+    d.dtype = 1
+    st, msg = status_of(lib, fn, ctypes.byref(d), FAKE, 3, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 4 and "bf16" in msg
+    d = good_desc()
+    d.cu_q = d.cu_k = FAKE
+    st, msg = status_of(lib, fn, ctypes.byref(d), FAKE, 3, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 4 and "dense" in msg
