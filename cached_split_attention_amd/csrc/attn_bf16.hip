@@ -620,7 +620,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   int bid = (int)blockIdx.x;
   if constexpr (GATE) {
     if (bid < grid_g) {
-      gate::run(gp, bid, smem);
+      gate::run<false>(gp, bid, smem);
       return;
     }
     bid -= grid_g;
@@ -818,7 +818,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   int bid = (int)blockIdx.x;
   if constexpr (GATE) {
     if (bid < grid_g) {
-      gate::run(gp, bid, smem);
+      gate::run<true>(gp, bid, smem);
       return;
     }
     bid -= grid_g;
@@ -1153,9 +1153,23 @@ int max_splits_bf16(int d, int variant) {
 }
 
 hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, const AttnParams* p1, int d,
-                            hipStream_t s, const GateParams* g) {
-  if (g && !p1) return hipErrorInvalidValue;
+                            hipStream_t s, const GateParams* g_in) {
+  if (g_in && !p1) return hipErrorInvalidValue;
   Bf16Plan plan = plan_in;
+  // In the 256-row kernel every gate workgroup is as heavy as an attention
+  // one (a whole CU's LDS), so the count gates take several positions per
+  // workgroup there: about 64 workgroups in all.
+  GateParams g_multi;
+  const GateParams* g = g_in;
+  if (g_in && plan.variant == 3 && g_in->mode != BA_GATE_COSINE) {
+    g_multi = *g_in;
+    const int64_t positions = (int64_t)g_in->n_blk * g_in->n_seq;
+    int64_t ppw = (positions + 63) / 64;
+    if (ppw < 1) ppw = 1;
+    if (ppw > kMaxGatePositions) ppw = kMaxGatePositions;
+    g_multi.pos_per_wg = (int)ppw;
+    g = &g_multi;
+  }
   // 32-key single-wave ring: in-block attention only
   if (plan.variant == 2 && (p.mode != kBlock || (p1 && p1->mode != kBlock))) plan.variant = 1;
   if (d == 128) {

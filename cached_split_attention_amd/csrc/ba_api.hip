@@ -510,6 +510,7 @@ ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint
   p.gamma = g->gamma;
   p.cache_valid = g->cache_valid ? 1 : 0;
   p.since = g->mode == BA_GATE_COUNT_CUM ? g->since_refresh : nullptr;
+  p.pos_per_wg = 1;
   p.chunks = count ? 1 : ba::gate_cos_chunks(g->n_blk, g->d);
   bool v16 = (g->d * p.esize) % 16 == 0;
   const void* ptrs[6] = {g->q_cur, g->q_prev, g->k_cur, g->k_prev, g->v_cur, g->v_prev};
@@ -590,6 +591,7 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
   }
   const size_t own = ba::gate_workspace_bytes(gate->mode, gate->n_seq, gate->hq, gate->n_blk, gate->d);
   gp.ready = reinterpret_cast<int32_t*>(static_cast<char*>(gate_workspace) + ((own + 127) & ~(size_t)127));
+
   gp.ready_stride = (int)ready_stride_ints(gate);
   return split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &gp);
 }

@@ -129,8 +129,10 @@ struct GateParams {
   int32_t* ready;      // NULL, or the ready words (kReadyCopies copies)
   int ready_stride;    // ints between copies
   uint8_t* since;      // cumulative count mode: positions updated since the last refresh
+  int pos_per_wg;      // count modes: block positions per workgroup (1 .. 32)
 };
 constexpr int kReadyCopies = 4;
+constexpr int kMaxGatePositions = 32;   // count-gate positions per workgroup (one mask bit each)
 int gate_grid(const GateParams& p);
 
 // One launch; with p1 non-NULL it also runs the independent part p1 (same

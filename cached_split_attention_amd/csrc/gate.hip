@@ -11,8 +11,8 @@ namespace {
 
 template <typename W>
 __global__ void __launch_bounds__(256) gate_count_kernel(const GateParams p) {
-  __shared__ int s_m;
-  gate::count_body<W>(p, blockIdx.x, blockIdx.y, &s_m);
+  __shared__ unsigned s_scratch[4];
+  gate::count_body<W, false>(p, blockIdx.x, s_scratch);
 }
 
 __global__ void __launch_bounds__(256) gate_cos_kernel(const GateParams p) {
@@ -39,13 +39,14 @@ size_t gate_workspace_bytes(int mode, int n_seq, int hq, int n_blk, int d) {
 }
 
 int gate_grid(const GateParams& p) {
-  return p.mode != BA_GATE_COSINE ? p.n_blk * p.n_seq : p.chunks * p.hq * p.n_seq;
+  if (p.mode != BA_GATE_COSINE) return (p.n_blk + p.pos_per_wg - 1) / p.pos_per_wg * p.n_seq;
+  return p.chunks * p.hq * p.n_seq;
 }
 
 hipError_t launch_gate(const GateParams& p, hipStream_t s) {
   if (p.n_seq == 0 || p.n_blk == 0) return hipSuccess;
   if (p.mode != BA_GATE_COSINE) {
-    dim3 grid(p.n_blk, p.n_seq);
+    dim3 grid(gate_grid(p));
     if (p.vec16)
       hipLaunchKernelGGL(gate_count_kernel<gate::u32x4>, grid, dim3(256), 0, s, p);
     else if (p.esize == 4)

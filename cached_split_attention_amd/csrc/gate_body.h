@@ -74,8 +74,7 @@ __device__ __forceinline__ bool words_differ(const W& x, const W& y) {
 // prev?  The position's words (Q heads, then K heads, then V heads; W = the
 // comparison word) are spread over the workgroup, 16 per thread per round,
 // with all of a round's loads issued before any comparison so a round costs
-// one memory latency (one round covers 64 KB of cur and of prev at 256
-// threads and 16-byte words).
+// one memory latency.
 template <typename W>
 __device__ bool position_changed(const GateParams& p, int b, int pos) {
   const int wpr = p.d * p.esize / (int)sizeof(W);
@@ -118,40 +117,128 @@ __device__ bool position_changed(const GateParams& p, int b, int pos) {
   return diff;
 }
 
-// Count gate (and its cumulative and per-row forms), one workgroup per
-// (block position pos, sequence b).  s_m: one int of LDS.
+// Which of the block positions pos0 .. pos0+npos-1 of sequence b have a Q, K
+// or V row that differs between cur and prev?  Returns this thread's share
+// as a bit mask (bit i: position pos0+i).  The positions' words (per
+// position: Q heads, then K heads, then V heads; W = the comparison word) are
+// spread over the workgroup, U per thread per round, with all of a round's
+// loads issued before any comparison, so a round costs one memory latency
+// (one round covers 64 KB of cur and of prev at 256 threads and 16-byte
+// words).
 template <typename W>
-__device__ void count_body(const GateParams& p, int pos, int b, int* s_m) {
-  const int64_t pe = (int64_t)b * p.n_blk + pos;
-  bool diff = false;
-  if (p.upd_mask) {
-    diff = threadIdx.x == 0 && p.upd_mask[pe] != 0;
-  } else {
-    diff = position_changed<W>(p, b, pos);
+__device__ unsigned positions_changed(const GateParams& p, int b, int pos0, int npos) {
+  const int wpr = p.d * p.esize / (int)sizeof(W);
+  const int nq = p.hq * wpr;
+  const int nk = p.k_cur ? p.hkv * wpr : 0;
+  const int nv = p.v_cur ? p.hkv * wpr : 0;
+  const int per_pos = nq + nk + nv;
+  const int total = npos * per_pos;
+  constexpr int U = 16;
+  unsigned mask = 0;
+  for (int t0 = threadIdx.x; t0 < total; t0 += U * (int)blockDim.x) {
+    W x[U], y[U];
+    int pi[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int w = t0 + u * (int)blockDim.x;
+      x[u] = W{};
+      y[u] = W{};
+      pi[u] = 0;
+      if (w < total) {
+        const int i = w / per_pos;
+        w -= i * per_pos;
+        pi[u] = i;
+        const void* cur = p.q_cur;
+        const void* prev = p.q_prev;
+        int64_t s0 = p.qs0, s1 = p.qs1, s2 = p.qs2;
+        if (w >= nq) {
+          w -= nq;
+          const bool isv = w >= nk;
+          if (isv) w -= nk;
+          cur = isv ? p.v_cur : p.k_cur;
+          prev = isv ? p.v_prev : p.k_prev;
+          s0 = p.ks0;
+          s1 = p.ks1;
+          s2 = p.ks2;
+        }
+        const int hh = w / wpr, wi = w - hh * wpr;
+        const int64_t off = ((int64_t)b * s0 + (int64_t)(pos0 + i) * s1 + (int64_t)hh * s2) * p.esize;
+        x[u] = reinterpret_cast<const W*>(static_cast<const char*>(cur) + off)[wi];
+        y[u] = reinterpret_cast<const W*>(static_cast<const char*>(prev) + off)[wi];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (words_differ(x[u], y[u])) mask |= 1u << pi[u];
   }
-  diff = __syncthreads_or(diff);
-  // One atomic per workgroup carries both the ticket (low 16 bits) and the
-  // count of changed positions (high 16 bits); the last workgroup of the
-  // sequence reads the total from its own return value and resets the word.
-  if (threadIdx.x == 0) {
+  return mask;
+}
+
+// Count gate (and its cumulative and per-row forms), one workgroup per
+// p.pos_per_wg consecutive block positions of one sequence (workgroup wg:
+// sequence wg / n, group wg % n, n groups per sequence).  lds: two unsigned
+// and one int of scratch.
+template <typename W, bool MULTI>
+__device__ void count_body(const GateParams& p, int wg, void* lds) {
+  const int ppw = MULTI ? p.pos_per_wg : 1;
+  const int nw = MULTI ? (p.n_blk + ppw - 1) / ppw : p.n_blk;
+  const int b = wg / nw, grp = wg - b * nw;
+  const int pos0 = grp * ppw, npos = MULTI ? min(ppw, p.n_blk - pos0) : 1;
+  unsigned* s_mask = static_cast<unsigned*>(lds);   // [0]: changed, [1]: counted
+  int* s_m = reinterpret_cast<int*>(s_mask + 2);
+  // Per position: the mark (cumulative mode) or the row decision (rows
+  // mode), stored and acknowledged before the ticket below, so that a clear
+  // by the finishing workgroup lands after it; returns whether it counts.
+  auto settle = [&](int i, bool d) {
+    const int64_t pe = (int64_t)b * p.n_blk + pos0 + i;
     if (p.mode == BA_GATE_COUNT_CUM) {
       // marked if updated at any step since the last refresh (with no
-      // valid cache there is none: old marks do not count); the mark is
-      // stored before the ticket so that a clear by the finishing
-      // workgroup lands after it
-      diff = diff || (p.cache_valid && ld_agent(p.since + pe) != 0);
-      st_agent(p.since + pe, (uint8_t)(diff ? 1 : 0));
+      // valid cache there is none: old marks do not count)
+      d = d || (p.cache_valid && ld_agent(p.since + pe) != 0);
+      st_agent(p.since + pe, (uint8_t)(d ? 1 : 0));
       stores_done();
     } else if (p.mode == BA_GATE_ROWS) {
-      st_agent(p.decision + pe, (uint8_t)(p.cache_valid && !diff ? 1 : 0));
+      st_agent(p.decision + pe, (uint8_t)(p.cache_valid && !d ? 1 : 0));
     }
-    const unsigned old = atomicAdd(reinterpret_cast<unsigned*>(p.ws_int) + b, (diff ? 0x10000u : 0u) + 1u);
+    return d;
+  };
+  int c = 0;   // positions of this workgroup that count (thread 0)
+  if (!MULTI || npos == 1) {
+    // one position: a single word scan and a workgroup OR
+    bool diff = false;
+    if (p.upd_mask) diff = threadIdx.x == 0 && p.upd_mask[(int64_t)b * p.n_blk + pos0] != 0;
+    else diff = position_changed<W>(p, b, pos0);
+    diff = __syncthreads_or(diff);
+    if (threadIdx.x == 0) c = settle(0, diff) ? 1 : 0;
+  } else {
+    if (threadIdx.x < 2) s_mask[threadIdx.x] = 0u;
+    __syncthreads();
+    unsigned mine = 0;
+    if (p.upd_mask) {
+      if ((int)threadIdx.x < npos && p.upd_mask[(int64_t)b * p.n_blk + pos0 + threadIdx.x] != 0)
+        mine = 1u << threadIdx.x;
+    } else {
+      mine = positions_changed<W>(p, b, pos0, npos);
+    }
+    if (mine) atomicOr(s_mask, mine);
+    __syncthreads();
+    // (threads i < npos <= 32 are all in the first wave)
+    const int i = threadIdx.x;
+    if (i < npos && settle(i, (s_mask[0] >> i) & 1u)) atomicOr(s_mask + 1, 1u << i);
+    __syncthreads();
+    if (threadIdx.x == 0) c = __popc(s_mask[1]);
+  }
+  // One atomic per workgroup carries both the ticket (low 16 bits) and the
+  // count of counted positions (high 16 bits); the last workgroup of the
+  // sequence reads the total from its own return value and resets the word.
+  if (threadIdx.x == 0) {
+    const unsigned old = atomicAdd(reinterpret_cast<unsigned*>(p.ws_int) + b, ((unsigned)c << 16) + 1u);
     *s_m = -1;
-    if ((int)(old & 0xffffu) == p.n_blk - 1) {
-      const int m = (int)(old >> 16) + (diff ? 1 : 0);
+    if ((int)(old & 0xffffu) == nw - 1) {
+      const int m = (int)(old >> 16) + c;
       *s_m = m;
       if (p.ready)
-        for (int c = 0; c < kReadyCopies; ++c) atomicExch(p.ready + c * p.ready_stride + b, kCountReady | m);
+        for (int k = 0; k < kReadyCopies; ++k) atomicExch(p.ready + k * p.ready_stride + b, kCountReady | m);
       atomicExch(p.ws_int + b, 0);
       p.m_count[b] = m;
     }
@@ -241,18 +328,18 @@ __device__ void cos_body(const GateParams& p, int c, int h, int b, double* red) 
 }
 
 // Gate workgroup wg of a grid of gate_grid(p) workgroups (count modes:
-// position fastest, then sequence; cosine: chunk, head, sequence); lds is scratch of
-// at least 3 * blockDim.x doubles.
+// position group fastest, then sequence; cosine: chunk, head, sequence); lds is scratch of
+// at least 3 * blockDim.x doubles.  MULTI: the count modes may take several
+// positions per workgroup (p.pos_per_wg); otherwise p.pos_per_wg must be 1.
+template <bool MULTI>
 __device__ __forceinline__ void run(const GateParams& p, int wg, void* lds) {
   if (p.mode != BA_GATE_COSINE) {
-    const int pos = wg % p.n_blk, b = wg / p.n_blk;
-    int* s_m = static_cast<int*>(lds);
     if (p.vec16)
-      count_body<u32x4>(p, pos, b, s_m);
+      count_body<u32x4, MULTI>(p, wg, lds);
     else if (p.esize == 4)
-      count_body<uint32_t>(p, pos, b, s_m);
+      count_body<uint32_t, MULTI>(p, wg, lds);
     else
-      count_body<uint16_t>(p, pos, b, s_m);
+      count_body<uint16_t, MULTI>(p, wg, lds);
   } else {
     const int c = wg % p.chunks, h = (wg / p.chunks) % p.hq, b = wg / (p.chunks * p.hq);
     cos_body(p, c, h, b, static_cast<double*>(lds));
