@@ -267,16 +267,60 @@ __device__ void cos_body(const GateParams& p, int c, int h, int b, double* red) 
   const int nt = (int)blockDim.x, t = (int)threadIdx.x;
   const int per = (p.n_blk + p.chunks - 1) / p.chunks;
   const int p0 = min(p.n_blk, c * per), p1 = min(p.n_blk, p0 + per);
-  const int n = (p1 - p0) * p.d;
   double dot = 0.0, nc = 0.0, np = 0.0;
-  for (int e = t; e < n; e += nt) {
-    const int pos = p0 + e / p.d, dd = e - (e / p.d) * p.d;
-    const int64_t idx = (int64_t)b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + dd;
-    const double x = load_elem(p.q_cur, idx, p.esize);
-    const double y = load_elem(p.q_prev, idx, p.esize);
-    dot = fma(x, y, dot);
-    nc = fma(x, x, nc);
-    np = fma(y, y, np);
+  if (p.vec16) {
+    // 16-byte words (8 bf16 or 4 float32 of one row), U per thread issued
+    // together before any is summed; each thread sums its words in order
+    constexpr int U = 4;
+    const int ve = 16 / p.esize, wpr = p.d / ve;
+    const int n = (p1 - p0) * wpr;
+    for (int w0 = t; w0 < n; w0 += U * nt) {
+      u32x4 xw[U], yw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int w = w0 + u * nt;
+        xw[u] = yw[u] = u32x4{0, 0, 0, 0};
+        if (w < n) {
+          const int pos = p0 + w / wpr, cw = w - (w / wpr) * wpr;
+          const int64_t idx = (int64_t)b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + (int64_t)cw * ve;
+          xw[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q_cur) + idx * p.esize);
+          yw[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q_prev) + idx * p.esize);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (w0 + u * nt >= n) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (p.esize == 2) {
+            const double x0 = __uint_as_float(xw[u][j] << 16), x1 = __uint_as_float(xw[u][j] & 0xffff0000u);
+            const double y0 = __uint_as_float(yw[u][j] << 16), y1 = __uint_as_float(yw[u][j] & 0xffff0000u);
+            dot = fma(x0, y0, dot);
+            nc = fma(x0, x0, nc);
+            np = fma(y0, y0, np);
+            dot = fma(x1, y1, dot);
+            nc = fma(x1, x1, nc);
+            np = fma(y1, y1, np);
+          } else {
+            const double x0 = __uint_as_float(xw[u][j]), y0 = __uint_as_float(yw[u][j]);
+            dot = fma(x0, y0, dot);
+            nc = fma(x0, x0, nc);
+            np = fma(y0, y0, np);
+          }
+        }
+      }
+    }
+  } else {
+    const int n = (p1 - p0) * p.d;
+    for (int e = t; e < n; e += nt) {
+      const int pos = p0 + e / p.d, dd = e - (e / p.d) * p.d;
+      const int64_t idx = (int64_t)b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + dd;
+      const double x = load_elem(p.q_cur, idx, p.esize);
+      const double y = load_elem(p.q_prev, idx, p.esize);
+      dot = fma(x, y, dot);
+      nc = fma(x, x, nc);
+      np = fma(y, y, np);
+    }
   }
   red[t] = dot;
   red[nt + t] = nc;
