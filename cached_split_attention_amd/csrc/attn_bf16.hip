@@ -1157,17 +1157,26 @@ hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, const 
   if (g_in && !p1) return hipErrorInvalidValue;
   Bf16Plan plan = plan_in;
   // In the 256-row kernel every gate workgroup is as heavy as an attention
-  // one (a whole CU's LDS), so the count gates take several positions per
-  // workgroup there: about 64 workgroups in all.
+  // one (a whole CU's LDS), so the gates there use fewer, longer
+  // workgroups: the count gates several positions per workgroup (about 64
+  // workgroups in all), the cosine gate fewer position chunks per (sequence,
+  // head) (about 128 workgroups; its workspace is sized for the most chunks).
   GateParams g_multi;
   const GateParams* g = g_in;
-  if (g_in && plan.variant == 3 && g_in->mode != BA_GATE_COSINE) {
+  if (g_in && plan.variant == 3) {
     g_multi = *g_in;
-    const int64_t positions = (int64_t)g_in->n_blk * g_in->n_seq;
-    int64_t ppw = (positions + 63) / 64;
-    if (ppw < 1) ppw = 1;
-    if (ppw > kMaxGatePositions) ppw = kMaxGatePositions;
-    g_multi.pos_per_wg = (int)ppw;
+    if (g_in->mode != BA_GATE_COSINE) {
+      const int64_t positions = (int64_t)g_in->n_blk * g_in->n_seq;
+      int64_t ppw = (positions + 63) / 64;
+      if (ppw < 1) ppw = 1;
+      if (ppw > kMaxGatePositions) ppw = kMaxGatePositions;
+      g_multi.pos_per_wg = (int)ppw;
+    } else {
+      const int64_t heads = (int64_t)g_in->hq * g_in->n_seq;
+      int64_t ch = 128 / (heads > 0 ? heads : 1);
+      if (ch < 1) ch = 1;
+      if (ch < g_in->chunks) g_multi.chunks = (int)ch;
+    }
     g = &g_multi;
   }
   // 32-key single-wave ring: in-block attention only
