@@ -367,7 +367,8 @@ def run_varlen(args):
 
     s_bytes, s_flops, p_bytes, p_flops = varlen_work(vb, n_total)
     roof, achieved, achieved_tf = roofline_of(p_bytes, p_flops, pref_us)
-    roof = with_measured(roof, measured_peaks(dev))
+    if not args.no_peaks:
+        roof = with_measured(roof, measured_peaks(dev))
     out = {
         "metric": METRIC,
         "value": round(s_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -617,7 +618,8 @@ def run_kl(args):
     us = e0.elapsed_time(e1) * 1e3 / (args.steps * n_copies)
     nbytes = pair_bytes + KL_ROWS * (4 + 1 + 1)
     roof, achieved, _ = roofline_of(nbytes, 1, us)
-    roof = with_measured(roof, measured_peaks(dev))
+    if not args.no_peaks:
+        roof = with_measured(roof, measured_peaks(dev))
     out = {
         "metric": METRIC, "value": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": 1, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True,
@@ -657,6 +659,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2_llada")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy and GEMM peaks (kernel traces of the path alone)")
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated prefix copies")
     ap.add_argument("--lp", type=int, default=None,
                     help="prefix length override for the dense shapes (long-context sweep)")
@@ -787,7 +791,8 @@ def main():
     p_bytes1, p_flops1 = work[0][2], work[0][3]
     traffic = measured_traffic(args.workload)
     roof, achieved, achieved_tf = roofline_of(p_bytes1, p_flops1, pref_mean_us)
-    roof = with_measured(roof, measured_peaks(dev))
+    if not args.no_peaks:
+        roof = with_measured(roof, measured_peaks(dev))
 
     out = {
         "metric": METRIC,
