@@ -204,12 +204,16 @@ __device__ void count_body(const GateParams& p, int wg, void* lds) {
   };
   int c = 0;   // positions of this workgroup that count (thread 0)
   if (!MULTI || npos == 1) {
-    // one position: a single word scan and a workgroup OR
+    // one position: a single word scan and a workgroup OR through the
+    // scratch (not __syncthreads_or, which brings LDS of its own)
+    if (threadIdx.x == 0) s_mask[0] = 0u;
+    __syncthreads();
     bool diff = false;
     if (p.upd_mask) diff = threadIdx.x == 0 && p.upd_mask[(int64_t)b * p.n_blk + pos0] != 0;
     else diff = position_changed<W>(p, b, pos0);
-    diff = __syncthreads_or(diff);
-    if (threadIdx.x == 0) c = settle(0, diff) ? 1 : 0;
+    if (diff) s_mask[0] = 1u;
+    __syncthreads();
+    if (threadIdx.x == 0) c = settle(0, s_mask[0] != 0u) ? 1 : 0;
   } else {
     if (threadIdx.x < 2) s_mask[threadIdx.x] = 0u;
     __syncthreads();

@@ -447,6 +447,35 @@ def test_prefix_attn(dtype, shape):
     assert torch.equal(a, a2) and torch.equal(l, l2)
 
 
+@pytest.mark.parametrize("offset", [-10.0, -5.0])
+@pytest.mark.parametrize("shape", [DENSE_SHAPES[0], DENSE_SHAPES[1], DENSE_SHAPES[2], DENSE_SHAPES[6],
+                                   DENSE_SHAPES[9]])
+def test_prefix_attn_score_jumps(offset, shape):
+    """Scores that jump far above the running reference mid-row.  Prefix keys
+    come in 96-key stripes; every other stripe (the first included) is
+    shifted by `offset` along the queries' mean direction, so scores jump by
+    about 80 (offset -10) or 40 (offset -5) log2 units between stripes.  A
+    split whose first tile is in a low stripe then meets scores whose
+    exponentials under the reference overflow a tile sum of 2^64 (the tile
+    is redone under its maximum) or reach about 2^40 (kept as they are)."""
+    from workloads import bf16_bits_to_f32
+    B, hq, hkv, d, lp, nb = shape
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=31 + int(-offset))
+    kp = bf16_bits_to_f32(s.kp) * np.float32(0.3)
+    kp[:, :, (np.arange(lp) // 96) % 2 == 0, :] += np.float32(offset)
+    s.kp = round_to_bf16_bits(kp)
+    s.q[0] = round_to_bf16_bits(bf16_bits_to_f32(s.q[0]) * np.float32(0.3) + np.float32(0.5))
+    want_a, want_l = _oracle_prefix(s)
+    q, kp_d, vp_d = dev_bits(s.q[0]), dev_bits(s.kp), dev_bits(s.vp)
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q, kp_d, vp_d)), device=DEV, dtype=torch.uint8)
+    a = torch.full((B * nb, hq, d), 777.0, device=DEV)
+    l = torch.full((B * nb, hq), 777.0, device=DEV)
+    ba.ba_prefix_attn(q, kp_d, vp_d, a, l, ws)
+    torch.cuda.synchronize()
+    check_a(host(a), want_a, "A_out")
+    check_l(host(l), want_l, "L_out")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(3, 6, 2, 128, 900, 33), (3, 8, 2, 128, 700, 70)])
 def test_prefix_attn_decision_leaves_cache_untouched(dtype, shape):
