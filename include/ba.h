@@ -50,7 +50,7 @@ typedef enum {
   BA_ERR_NULL = 1,        /* a required pointer is NULL                     */
   BA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes / strides  */
   BA_ERR_DTYPE = 3,       /* unknown dtype                                 */
-  BA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement   */
+  BA_ERR_UNSUPPORTED = 4, /* valid request the library does not implement  */
   BA_ERR_WORKSPACE = 5,   /* workspace missing or too small                */
   BA_ERR_HIP = 6          /* a HIP launch reported an error                */
 } ba_status;
