@@ -95,7 +95,11 @@ struct PrefixPlan {
 
 // n_kblocks >= 0: key-block list mode, one iteration tile per listed block
 // and at most 64 list entries per workgroup; chunk then counts entries.
-PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1) {
+// partial: the call is gated per head (cosine gate with a valid cache), so
+// an unknown share of the work items recomputes; the makespan estimate is
+// then averaged over shares 1/8, 2/8, .., 1 instead of taken at 1 (smaller
+// splits keep a step that recomputes few heads short).
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, bool partial = false) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
     pp.row_tiles = 1;
@@ -122,12 +126,17 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1) {
   if (max_s > lds_cap) max_s = lds_cap;
   int64_t best_s = 1;
   double best_cost = 1e300;
+  const int shares = partial ? 8 : 1;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
-    const int64_t rounds = (items * se + slots - 1) / slots;
+    double span = 0.0;
+    for (int k = shares; k >= 1; --k) {
+      const int64_t it = (items * k + shares - 1) / shares;
+      span += (double)((it * se + slots - 1) / slots) * (double)(ci + 2);
+    }
     const double comb = se > 1 ? 2.0 + 2.0 * (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
-    const double cost = (double)rounds * (double)(ci + 2) + comb;
+    const double cost = span / shares + comb;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_s = se;
@@ -196,10 +205,14 @@ int32_t ba_debug_set_gate_spin_limit(int32_t polls) {
   return prev;
 }
 
+// Covers both plans a descriptor can get (ungated or count-gated, and
+// per-head gated in ba_gated_split_attn).
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
-  return prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
+  const size_t full = prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
+  const size_t part = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, true));
+  return full > part ? full : part;
 }
 
 namespace {
@@ -222,7 +235,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
-  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1);
+  const bool per_head = gate != nullptr && gate->mode == BA_GATE_COSINE && desc->decision != nullptr;
+  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, per_head && !kblocks);
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
