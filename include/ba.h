@@ -104,7 +104,9 @@ typedef struct ba_attn_desc {
  * prefix gives A_out = 0, L_out = -inf.
  * The key range is split across workgroups; partial results go to
  * `workspace`, whose size ba_prefix_attn_workspace() returns (0 means none is
- * needed and workspace may be NULL).  The workspace needs no
+ * needed and workspace may be NULL).  That size covers every call that takes
+ * this descriptor's prefix workspace (a per-head gated fused step may split
+ * the keys more finely than the other calls).  The workspace needs no
  * initialisation; calls that overlap in time must not share one.
  */
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc);
