@@ -42,10 +42,12 @@
 //                     group's wave on a SIMD issues MFMAs the other's issues
 //                     the exponentials, so the matrix cores are not left idle
 //                     during the softmax.  Serves long row counts.
-// Work mapping: work items are numbered so that the row tiles and key splits
-// sharing one (sequence, KV head) are consecutive, and consecutive items go
-// to the same XCD (workgroup i runs on XCD i % 8), so K/V re-reads hit that
-// XCD's L2.
+// Work mapping: workgroup i runs on XCD i % 8.  Work items are groups
+// (key split, sequence, KV head), split fastest, each with its row tiles;
+// group g goes to XCD g % 8 and its row tiles (which read the same K/V
+// tiles) to consecutive workgroups there, so their re-reads hit that XCD's
+// L2, while the groups of any subset of sequences or heads -- what a gated
+// step recomputes -- spread over all XCDs.
 
 #include <math.h>
 
@@ -500,14 +502,13 @@ struct Item {
 template <int ROWS>
 __device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   Item it{};
-  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int item = (wg % kXcds) * per_xcd + wg / kXcds;
+  const int j = wg / kXcds;
+  const int g = (j / p.row_tiles) * kXcds + wg % kXcds;   // group: (split, sequence, KV head)
   it.valid = false;
-  if (item >= n_items) return it;
-  it.split = item % p.n_splits;
-  it.rt = (item / p.n_splits) % p.row_tiles;
-  const int bz = item / (p.n_splits * p.row_tiles);
+  if (g >= p.n_splits * p.n_seq * p.hkv) return it;
+  it.split = g % p.n_splits;
+  it.rt = j % p.row_tiles;
+  const int bz = g / p.n_splits;
   it.b = bz / p.hkv;
   it.kvh = bz - it.b * p.hkv;
   it.qbase = 0;
@@ -1069,10 +1070,11 @@ hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
 
 namespace {
 
+// Groups (split, sequence, KV head) are dealt to the XCDs in turn, each with
+// its row tiles on consecutive workgroups of its XCD (decode_item).
 int item_grid(const AttnParams& p) {
-  const int n_items = p.n_splits * p.row_tiles * p.n_seq * p.hkv;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  return per_xcd * kXcds;
+  const int n_groups = p.n_splits * p.n_seq * p.hkv;
+  return kXcds * ((n_groups + kXcds - 1) / kXcds) * p.row_tiles;
 }
 
 // p1 == nullptr: one part.  With two parts, p1's workgroups come first in

@@ -95,11 +95,11 @@ struct PrefixPlan {
 
 // n_kblocks >= 0: key-block list mode, one iteration tile per listed block
 // and at most 64 list entries per workgroup; chunk then counts entries.
-// partial: the call is gated per head (cosine gate with a valid cache), so
-// an unknown share of the work items recomputes; the makespan estimate is
-// then averaged over shares 1/8, 2/8, .., 1 instead of taken at 1 (smaller
-// splits keep a step that recomputes few heads short).
-PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, bool partial = false) {
+// shares > 1: the call is gated (valid cache), so an unknown share of the
+// work items recomputes; the makespan estimate is then averaged over shares
+// 1/shares, 2/shares, .., 1 instead of taken at 1 (smaller splits keep a
+// step that recomputes few heads or sequences short).
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 1) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
     pp.row_tiles = 1;
@@ -126,7 +126,7 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, boo
   if (max_s > lds_cap) max_s = lds_cap;
   int64_t best_s = 1;
   double best_cost = 1e300;
-  const int shares = partial ? 8 : 1;
+  if (shares < 1) shares = 1;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
@@ -205,14 +205,31 @@ int32_t ba_debug_set_gate_spin_limit(int32_t polls) {
   return prev;
 }
 
-// Covers both plans a descriptor can get (ungated or count-gated, and
-// per-head gated in ba_gated_split_attn).
+namespace {
+
+// Recomputing shares the split planner averages over for a gated fused step
+// (valid cache): per head for the cosine gate, per sequence for the count
+// gates; 1 otherwise.
+int gate_shares(const ba::GateParams* gate, const ba_attn_desc* desc) {
+  if (!gate || !desc->decision) return 1;
+  if (gate->mode == BA_GATE_COSINE) return 8;
+  return desc->n_seq < 8 ? (desc->n_seq > 1 ? desc->n_seq : 1) : 8;
+}
+
+}  // namespace
+
+// Covers every plan a descriptor can get (ungated, and the gated fused
+// step's, whose split count depends on the gate mode).
 size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
-  const size_t full = prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
-  const size_t part = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, true));
-  return full > part ? full : part;
+  size_t need = 0;
+  const int seq_shares = desc->n_seq < 8 ? (desc->n_seq > 1 ? desc->n_seq : 1) : 8;
+  for (int shares : {1, seq_shares, 8}) {
+    const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares));
+    if (b > need) need = b;
+  }
+  return need;
 }
 
 namespace {
@@ -235,8 +252,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
-  const bool per_head = gate != nullptr && gate->mode == BA_GATE_COSINE && desc->decision != nullptr;
-  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, per_head && !kblocks);
+  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 1 : gate_shares(gate, desc));
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
