@@ -97,8 +97,9 @@ struct PrefixPlan {
 // and at most 64 list entries per workgroup; chunk then counts entries.
 // shares > 1: the call is gated (valid cache), so an unknown share of the
 // work items recomputes; the makespan estimate is then averaged over shares
-// 1/shares, 2/shares, .., 1 instead of taken at 1 (smaller splits keep a
-// step that recomputes few heads or sequences short).
+// k/shares, k = 1 .. shares, weighted 1/k (a gate makes small recomputed
+// subsets the common case), instead of taken at the full share (smaller
+// splits keep a step that recomputes few heads or sequences short).
 PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 1) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
@@ -119,7 +120,8 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   // iteration tile of one workgroup: (rounds of workgroups over all slots) x
   // (tiles per workgroup + 2 for pipeline fill and epilogue), plus, with
   // more than one split, the combine launch (~2) and its traffic (partials
-  // written and read, relative to the K/V bytes all slots stream per tile).
+  // written and read, relative to the K/V bytes all slots stream per tile;
+  // the measured combine durations are about half of twice that ratio).
   const int64_t slots = 256LL * pp.bf.wg_per_cu;
   int64_t max_s = iters < 1 ? 1 : iters;
   const int64_t lds_cap = ba::max_splits_bf16(d->d, pp.bf.variant);
@@ -130,13 +132,14 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
-    double span = 0.0;
+    double span = 0.0, wsum = 0.0;
     for (int k = shares; k >= 1; --k) {
       const int64_t it = (items * k + shares - 1) / shares;
-      span += (double)((it * se + slots - 1) / slots) * (double)(ci + 2);
+      span += (double)((it * se + slots - 1) / slots) * (double)(ci + 2) / k;
+      wsum += 1.0 / k;
     }
-    const double comb = se > 1 ? 2.0 + 2.0 * (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
-    const double cost = span / shares + comb;
+    const double comb = se > 1 ? 2.0 + (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
+    const double cost = span / wsum + comb;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_s = se;
