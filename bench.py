@@ -163,7 +163,7 @@ def cpu_baseline(s, budget_s=20.0, got=None):
         runs += 1
         for t in range(1, s.steps + 1):
             total_bytes += step_work(s, ref[t]["gate"]["decision"])[0]
-        if time.perf_counter() - t0 >= budget_s / 2 or runs >= 50:
+        if time.perf_counter() - t0 >= budget_s / 2 or runs >= 1000:
             break
     dt = time.perf_counter() - t0
     out = {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
