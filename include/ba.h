@@ -293,7 +293,10 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos,
  * NULL), but in two launches instead of three: the gate's workgroups come
  * first in the attention launch and each gated prefix workgroup waits (with
  * agent-scope loads, bounded) until the gate has written its sequence's
- * decisions; the in-block part does not wait.
+ * decisions; the in-block part does not wait.  With a valid cache the key
+ * split is planned for a step that recomputes part of the heads or
+ * sequences, so it can be finer than ba_split_attn's; the outputs then agree
+ * with that sequence of calls up to the rounding of the split-KV combine.
  *   gate, m_count, cos, decision: as for ba_reuse_gate; gate->n_seq, hq,
  *     dtype and n_blk must equal prefix->n_seq, hq, dtype and max_q.
  *   gate_workspace: ba_gated_split_attn_gate_workspace(gate) bytes, zero-

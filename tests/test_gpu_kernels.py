@@ -705,6 +705,75 @@ def test_gated_split_attn(mode, shape):
 
 
 @pytest.mark.parametrize("mode", ["count", "cosine"])
+def test_gated_split_attn_finer_split(mode):
+    # With a valid cache the fused step plans its key split for a partly
+    # recomputing step, here 16 splits where the split pass takes 8 (eight
+    # sequences of 32 rows, 2048 prefix keys).  Decisions and M are the
+    # same; recomputed heads match the oracle's prefix attention, reused
+    # heads keep the cache bit for bit, and the merged output agrees with
+    # the split pass's to the parity bars (the two splits round P
+    # differently).
+    B, hq, hkv, d, lp, nb = 8, 8, 8, 128, 2048, 32
+    s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=95)
+    rows = B * nb
+    q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
+    kp, vp = dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
+    r = np.random.default_rng(6)
+    if mode == "count":
+        q_prev, k_prev, v_prev = q.clone(), k.clone(), v.clone()
+        for b in (1, 4, 6):   # these sequences recompute at tau = 4
+            for pos in range(5):
+                q_prev[b, pos] += 1.0
+        gate_kw, bmode, gkw = dict(tau=4), ba.BA_GATE_COUNT, dict(k_cur=k, k_prev=k_prev, v_cur=v, v_prev=v_prev)
+    else:
+        sig = torch.from_numpy(r.uniform(0.01, 0.8, size=(1, 1, hq, 1)).astype(np.float32)).to(DEV)
+        q_prev = (q.float() + sig * torch.randn(q.shape, device=DEV)).to(torch.bfloat16)
+        k_prev = v_prev = None
+        gate_kw, bmode, gkw = dict(gamma=0.9), ba.BA_GATE_COSINE, {}
+    cache_a = torch.from_numpy(r.standard_normal((rows, hq, d)).astype(np.float32)).to(DEV)
+    cache_l = torch.from_numpy(r.standard_normal((rows, hq)).astype(np.float32)).to(DEV)
+    nws = max(1, ba.ba_prefix_attn_workspace(q, kp, vp))
+
+    def buffers():
+        return dict(a_out=cache_a.clone(), l_out=cache_l.clone(), a_in=torch.empty(rows, hq, d, device=DEV),
+                    l_in=torch.empty(rows, hq, device=DEV), a_full=torch.empty(rows, hq, d, device=DEV),
+                    l_full=torch.empty(rows, hq, device=DEV), dec=torch.empty(B, hq, device=DEV, dtype=torch.uint8),
+                    m=torch.empty(B, device=DEV, dtype=torch.int32),
+                    cos=torch.empty(B, hq, device=DEV, dtype=torch.float64),
+                    ws=torch.zeros(nws, device=DEV, dtype=torch.uint8))
+
+    ref, fused = buffers(), buffers()
+    count = mode == "count"
+    gws_ref = torch.zeros(max(1, ba.ba_reuse_gate_workspace(bmode, q, q_prev, **gkw)), device=DEV, dtype=torch.uint8)
+    gws = torch.zeros(ba.ba_gated_split_attn_gate_workspace(bmode, q, q_prev, **gkw), device=DEV, dtype=torch.uint8)
+    ba.ba_reuse_gate(bmode, q, q_prev, decision=ref["dec"], workspace=gws_ref, cache_valid=True,
+                     m_count=ref["m"] if count else None, cos=None if count else ref["cos"], **gkw, **gate_kw)
+    ba.ba_split_attn(q, kp, vp, k, v, ref["a_out"], ref["l_out"], ref["a_in"], ref["l_in"], ref["a_full"],
+                     ref["l_full"], ref["ws"], decision=ref["dec"])
+    ba.ba_gated_split_attn(bmode, q_prev, kp, vp, k, v, fused["a_out"], fused["l_out"], fused["a_in"],
+                           fused["l_in"], fused["a_full"], fused["l_full"], fused["ws"], q=q, decision=fused["dec"],
+                           gate_workspace=gws, k_prev=k_prev, v_prev=v_prev, cache_valid=True,
+                           m_count=fused["m"] if count else None, cos=None if count else fused["cos"], **gate_kw)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["dec"], ref["dec"])
+    dv = host(ref["dec"])
+    assert 0 < dv.sum() < dv.size, "the decisions should mix reuse and recompute"
+    if count:
+        assert torch.equal(fused["m"], ref["m"])
+    reused = np.repeat(dv.astype(bool), nb, axis=0)   # [rows, hq]
+    a_out, l_out = host(fused["a_out"]), host(fused["l_out"])
+    assert np.array_equal(a_out[reused], host(cache_a)[reused])
+    assert np.array_equal(l_out[reused], host(cache_l)[reused])
+    want_a, want_l = _oracle_prefix(s)
+    check_a(a_out[~reused], want_a[~reused], "A_out (recomputed heads)")
+    check_l(l_out[~reused], want_l[~reused], "L_out (recomputed heads)")
+    assert torch.equal(fused["a_in"], ref["a_in"]) and torch.equal(fused["l_in"], ref["l_in"])
+    check_a(host(fused["a_full"]), host(ref["a_full"]), "A_full against the split pass")
+    check_l(host(fused["l_full"]), host(ref["l_full"]), "L_full against the split pass")
+    assert not host(gws).view(np.int32).any(), "gate workspace not left zero"
+
+
+@pytest.mark.parametrize("mode", ["count", "cosine"])
 def test_gated_split_attn_gives_up(mode):
     # The prefix workgroups' bounded wait for the gate, forced to give up at
     # once from the host (spin limit 0): every gated prefix workgroup counts
