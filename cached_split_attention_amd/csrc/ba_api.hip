@@ -119,9 +119,9 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   // Pick the key-split count minimising a makespan estimate in units of one
   // iteration tile of one workgroup: (rounds of workgroups over all slots) x
   // (tiles per workgroup + 2 for pipeline fill and epilogue), plus, with
-  // more than one split, the combine launch (~2) and its traffic (partials
-  // written and read, relative to the K/V bytes all slots stream per tile;
-  // the measured combine durations are about half of twice that ratio).
+  // more than one split, the combine launch (~2) and its traffic: the
+  // partial bytes relative to the K/V bytes all slots stream per tile, which
+  // matches the measured combine durations.
   const int64_t slots = 256LL * pp.bf.wg_per_cu;
   int64_t max_s = iters < 1 ? 1 : iters;
   const int64_t lds_cap = ba::max_splits_bf16(d->d, pp.bf.variant);
@@ -213,10 +213,15 @@ namespace {
 // Recomputing shares the split planner averages over for a gated fused step
 // (valid cache): per head for the cosine gate, per sequence for the count
 // gates; 1 otherwise.
+constexpr int kMaxShares = 8;
+
+// Shares for a gate that decides per sequence: one per sequence, at most
+// kMaxShares.
+int seq_shares(int n_seq) { return n_seq < 1 ? 1 : (n_seq < kMaxShares ? n_seq : kMaxShares); }
+
 int gate_shares(const ba::GateParams* gate, const ba_attn_desc* desc) {
   if (!gate || !desc->decision) return 1;
-  if (gate->mode == BA_GATE_COSINE) return 8;
-  return desc->n_seq < 8 ? (desc->n_seq > 1 ? desc->n_seq : 1) : 8;
+  return gate->mode == BA_GATE_COSINE ? kMaxShares : seq_shares(desc->n_seq);
 }
 
 }  // namespace
@@ -227,8 +232,7 @@ size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
   size_t need = 0;
-  const int seq_shares = desc->n_seq < 8 ? (desc->n_seq > 1 ? desc->n_seq : 1) : 8;
-  for (int shares : {1, seq_shares, 8}) {
+  for (int shares : {1, seq_shares(desc->n_seq), kMaxShares}) {
     const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares));
     if (b > need) need = b;
   }
