@@ -1160,16 +1160,17 @@ hipError_t launch_attn_bf16(const Bf16Plan& plan_in, const AttnParams& p, const 
   Bf16Plan plan = plan_in;
   // In the 256-row kernel every gate workgroup is as heavy as an attention
   // one (a whole CU's LDS), so the gates there use fewer, longer
-  // workgroups: the count gates several positions per workgroup (about 64
-  // workgroups in all), the cosine gate fewer position chunks per (sequence,
-  // head) (about 128 workgroups; its workspace is sized for the most chunks).
+  // workgroups: the count gates several positions per workgroup (about 128
+  // workgroups in all; 64 and 256 were slower on the GQA long-context step),
+  // the cosine gate fewer position chunks per (sequence, head) (about 128
+  // workgroups; its workspace is sized for the most chunks).
   GateParams g_multi;
   const GateParams* g = g_in;
   if (g_in && plan.variant == 3) {
     g_multi = *g_in;
     if (g_in->mode != BA_GATE_COSINE) {
       const int64_t positions = (int64_t)g_in->n_blk * g_in->n_seq;
-      int64_t ppw = (positions + 63) / 64;
+      int64_t ppw = (positions + 127) / 128;
       if (ppw < 1) ppw = 1;
       if (ppw > kMaxGatePositions) ppw = kMaxGatePositions;
       g_multi.pos_per_wg = (int)ppw;
