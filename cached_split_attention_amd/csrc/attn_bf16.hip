@@ -499,11 +499,19 @@ struct Item {
   bool valid;
 };
 
+// Work item group (key split, sequence, KV head; split fastest) of
+// workgroup wg: groups are dealt to the XCDs in turn, each with its row
+// tiles on consecutive workgroups of its XCD (workgroup i runs on XCD
+// i % kXcds).  A group past n_splits * n_seq * hkv is no work.
+__device__ __forceinline__ int item_group(const AttnParams& p, int wg) {
+  return (wg / kXcds / p.row_tiles) * kXcds + wg % kXcds;
+}
+
 template <int ROWS>
 __device__ __forceinline__ Item decode_item(const AttnParams& p, int wg) {
   Item it{};
   const int j = wg / kXcds;
-  const int g = (j / p.row_tiles) * kXcds + wg % kXcds;   // group: (split, sequence, KV head)
+  const int g = item_group(p, wg);   // (split, sequence, KV head)
   it.valid = false;
   if (g >= p.n_splits * p.n_seq * p.hkv) return it;
   it.split = g % p.n_splits;
@@ -828,6 +836,19 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   const AttnParams& p = second ? p1 : p0;
   const int wg = second ? bid - grid0 : bid;
   bool gated = p.decision != nullptr && p.mode != kBlock;
+  // A gated prefix workgroup reads its sequence's gate result first, from
+  // the prefix part's parameters alone (few dependent kernel-argument
+  // loads), and leaves at once when the whole sequence is reused: most
+  // prefix workgroups of a reuse step do only this.
+  int ready_r = -1;
+  if constexpr (GATE) {
+    if (second && p1.decision != nullptr && p1.ready != nullptr && p1.mode != kBlock) {
+      const int g = item_group(p1, wg);
+      if (g >= p1.n_splits * p1.n_seq * p1.hkv) return;
+      ready_r = gate_ready(p1, g / p1.n_splits / p1.hkv);
+      if (ready_r == 0) return;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -838,7 +859,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   if (!itm.valid) return;
   if constexpr (GATE) {
     if (gated && p.ready) {
-      const int r = gate_ready(p, itm.b);
+      const int r = ready_r >= 0 ? ready_r : gate_ready(p, itm.b);
       if (r == 0) return;
       gated = r == 2;
     }
