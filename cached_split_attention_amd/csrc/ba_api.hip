@@ -95,12 +95,15 @@ struct PrefixPlan {
 
 // n_kblocks >= 0: key-block list mode, one iteration tile per listed block
 // and at most 64 list entries per workgroup; chunk then counts entries.
-// shares > 1: the call is gated (valid cache), so an unknown share of the
+// shares >= 1: the call is gated (valid cache), so an unknown share of the
 // work items recomputes; the makespan estimate is then averaged over shares
 // k/shares, k = 1 .. shares, weighted 1/k (a gate makes small recomputed
-// subsets the common case), instead of taken at the full share (smaller
-// splits keep a step that recomputes few heads or sequences short).
-PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 1) {
+// subsets the common case; smaller splits keep a step that recomputes few
+// heads or sequences short), and over the step that recomputes nothing,
+// weighted 1, whose workgroups only read their decision and leave (about
+// half a tile each, per round of slots).  shares == 0: ungated, the full
+// share only.
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 0) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
     pp.row_tiles = 1;
@@ -128,7 +131,8 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   if (max_s > lds_cap) max_s = lds_cap;
   int64_t best_s = 1;
   double best_cost = 1e300;
-  if (shares < 1) shares = 1;
+  const bool gated = shares >= 1;
+  if (!gated) shares = 1;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
@@ -137,6 +141,10 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
       const int64_t it = (items * k + shares - 1) / shares;
       span += (double)((it * se + slots - 1) / slots) * (double)(ci + 2) / k;
       wsum += 1.0 / k;
+    }
+    if (gated) {
+      span += 0.5 * (double)((items * se + slots - 1) / slots);
+      wsum += 1.0;
     }
     const double comb = se > 1 ? 2.0 + (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
     const double cost = span / wsum + comb;
@@ -219,8 +227,9 @@ constexpr int kMaxShares = 8;
 // kMaxShares.
 int seq_shares(int n_seq) { return n_seq < 1 ? 1 : (n_seq < kMaxShares ? n_seq : kMaxShares); }
 
+// 0 (ungated) unless the call is a gated fused step with a valid cache.
 int gate_shares(const ba::GateParams* gate, const ba_attn_desc* desc) {
-  if (!gate || !desc->decision) return 1;
+  if (!gate || !desc->decision) return 0;
   return gate->mode == BA_GATE_COSINE ? kMaxShares : seq_shares(desc->n_seq);
 }
 
@@ -232,7 +241,7 @@ size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
   size_t need = 0;
-  for (int shares : {1, seq_shares(desc->n_seq), kMaxShares}) {
+  for (int shares : {0, seq_shares(desc->n_seq), kMaxShares}) {
     const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares));
     if (b > need) need = b;
   }
@@ -259,7 +268,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
-  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 1 : gate_shares(gate, desc));
+  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 0 : gate_shares(gate, desc));
   const size_t need = prefix_ws_bytes(desc, pp);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);

@@ -97,21 +97,21 @@ def test_prefix_workspace_required(lib):
 
 
 def test_prefix_workspace_covers_gated_split(lib):
-    # Eight sequences of 32 rows (8 heads) over 2048 prefix keys: the split
+    # Eight sequences of 16 rows (8 heads) over 4096 prefix keys: the split
     # pass plans 8 key splits, a gated fused step with a valid cache 16 (it
     # plans for a step that recomputes part of the sequences or heads).  The
     # workspace query covers the finer split: 16 x rows x heads x (d + 1)
     # float32 partials.
     d = lib_mod.AttnDesc()
-    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 8, 8, 8, 128, 32, 2048
+    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 8, 8, 8, 128, 16, 4096
     d.q = d.k = d.v = FAKE
-    for i, s in enumerate((32 * 8 * 128, 8 * 128, 128)):
+    for i, s in enumerate((16 * 8 * 128, 8 * 128, 128)):
         d.q_stride[i] = s
-    for i, s in enumerate((8 * 2048 * 128, 128, 2048 * 128)):
+    for i, s in enumerate((8 * 4096 * 128, 128, 4096 * 128)):
         d.k_stride[i] = s
         d.v_stride[i] = s
     need = lib.ba_prefix_attn_workspace(ctypes.byref(d))
-    assert need >= 16 * (8 * 32 * 8) * 129 * 4
+    assert need >= 16 * (8 * 16 * 8) * 129 * 4
 
 
 def test_prefix_empty_is_ok_without_launch(lib):

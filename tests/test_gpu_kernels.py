@@ -708,12 +708,12 @@ def test_gated_split_attn(mode, shape):
 def test_gated_split_attn_finer_split(mode):
     # With a valid cache the fused step plans its key split for a partly
     # recomputing step, here 16 splits where the split pass takes 8 (eight
-    # sequences of 32 rows, 2048 prefix keys).  Decisions and M are the
+    # sequences of 16 rows, 4096 prefix keys).  Decisions and M are the
     # same; recomputed heads match the oracle's prefix attention, reused
     # heads keep the cache bit for bit, and the merged output agrees with
     # the split pass's to the parity bars (the two splits round P
     # differently).
-    B, hq, hkv, d, lp, nb = 8, 8, 8, 128, 2048, 32
+    B, hq, hkv, d, lp, nb = 8, 8, 8, 128, 4096, 16
     s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=95)
     rows = B * nb
     q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
