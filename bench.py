@@ -1,24 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of cached split attention for block diffusion on one MI355X.
 
-Default workload: the LLaDA-8B-like attention shape (batch 1, 32 query heads
-on 32 KV heads, head dim 128, bf16, prefix 4096, block 32, 32 denoising steps
-per block, 1-2 tokens unmasked per step, count gate with tau = 4).  One bench
-step is one block's whole schedule: for every denoising step the reuse gate,
-the gate-predicated prefix (out-of-block) pass, and the in-block pass with
-the fused log-space merge.  The first denoising step of a block has no valid
+Default workload: the long-context grouped-query shape (batch 8, 32 query
+heads sharing 8 KV heads, head dim 128, bf16, prefix 32768, block 64, 64
+denoising steps per block, Poisson(3) rewritten block rows per step, count
+gate with tau = 8): the largest of the workload shapes.  One bench step is
+one block's whole schedule: for every denoising step the reuse gate, the
+gate-predicated prefix (out-of-block) pass, and the in-block pass with the
+fused log-space merge.  The first denoising step of a block has no valid
 cache and recomputes the prefix part.  Inputs are seeded synthetic tensors,
 resident in HBM before timing starts; the prefix K/V is rotated over copies
 totalling at least 1 GiB so a recompute reads it from HBM, not from the
 256 MB last-level cache.
 
 Prints one JSON line.  value = algorithmic bytes moved per second (GB/s);
-TFLOP/s, per-step latencies, the prefix kernel's roofline and the CPU
-oracle's rate on a bounded sample ride along.  --workload selects another of
-the workload shapes; the multi-branch varlen one (c5_varlen) times one step
-with a cold cache (varlen packing, then the split attention); kl_lock times
-the lock criterion; --lp and --sparse give the long-context and sparse
-residual-reuse legs of the dense shapes.
+TFLOP/s, per-step latencies, the prefix kernel's roofline, the in-block
+part's rate and the CPU oracle's rate on a bounded sample ride along.
+--workload selects another of the workload shapes (c2_llada: the LLaDA-like
+heads; c4_video; c1_tiny_f32); the multi-branch varlen one (c5_varlen) times
+one step with a cold cache (varlen packing, then the split attention);
+kl_lock times the lock criterion; --lp and --sparse give the long-context
+and sparse residual-reuse legs of the dense shapes.
 """
 
 from __future__ import annotations
@@ -144,40 +146,78 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(s, budget_s=20.0, got=None):
-    """The oracle on whole block schedules of the workload (timed), and, when
-    the GPU's final-step A_full/L_full are given, the errors the GPU path
-    achieves against the oracle's final step."""
-    import numpy as np
-    import oracle
+def host_cores():
+    """Cores this process may run on, the BLAS thread count and the CPU model."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = 1
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:  # noqa: BLE001
+        pass
+    return {"affinity_cores": affinity, "blas_threads": int(threads), "cpu_model": model or cpu_model()}
+
+
+def cpu_baseline(s, budget_s=12.0, got=None):
+    """The oracle, as it stands, on a bounded sample of the workload: whole
+    block schedules of one (sequence, query head) after another -- the gate
+    over the block, then per step the prefix part when that head recomputes,
+    the in-block part and the merge -- until budget_s has passed.  The rate
+    is the schedule's algorithmic bytes scaled to the pairs done.  When the
+    GPU's final-step A_full/L_full are given, the errors the GPU path
+    achieves on the sampled pairs are reported too."""
+    import numpy as np
+    import oracle
+    cores = host_cores()
     t0 = time.perf_counter()
-    runs = 0
-    total_bytes = 0
-    while True:
-        ref = oracle.run_block(s)
-        runs += 1
+    gates = oracle.step_gates(s)
+    pairs = [(b, h) for b in range(s.B) for h in range(s.hq)]
+    done = []
+    finals = {}
+    for b, h in pairs:
+        ao = lo = None
         for t in range(1, s.steps + 1):
-            total_bytes += step_work(s, ref[t]["gate"]["decision"])[0]
-        if time.perf_counter() - t0 >= budget_s / 2 or runs >= 1000:
+            if ao is None or gates[t]["decision"][b, h] == 0:
+                ao, lo = oracle.prefix_rows(s, t, b, h)
+            ai, li = oracle.block_rows(s, t, b, h)
+            af, lf = oracle.merge(ao, lo, ai, li)
+        finals[(b, h)] = (af, lf)
+        done.append((b, h))
+        if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    out = {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"{runs} full block schedule(s) of the same workload ({s.steps} steps each), "
-                     f"NumPy float64, {dt:.1f} s",
-           "ms_per_step": dt / runs * 1e3, "cpu_model": cpu_model()}
+    sched_bytes = sum(step_work(s, gates[t]["decision"])[0] for t in range(1, s.steps + 1))
+    frac = len(done) / len(pairs)
+    out = {"value": sched_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": cores["blas_threads"],
+           "kind": "oracle",
+           "sample": f"the whole {s.steps}-step block schedule (gate, prefix part on recomputing steps, "
+                     f"in-block part, merge) of {len(done)} of {len(pairs)} (sequence, query head) pairs, "
+                     f"bytes scaled to those pairs, NumPy float64, {dt:.1f} s",
+           "ms_per_step": dt / frac / s.steps * 1e3, **cores}
     if got is not None:
         ga, gl = got
-        wa, wl = ref[s.steps]["a_full"], ref[s.steps]["l_full"]
+        ga = ga.reshape(s.B, s.nb, s.hq, s.d)
+        gl = gl.reshape(s.B, s.nb, s.hq)
+        wa = np.stack([finals[p][0] for p in done])
+        wl = np.stack([finals[p][1] for p in done])
+        pa = np.stack([ga[b, :, h] for b, h in done])
+        pl = np.stack([gl[b, :, h] for b, h in done])
         out["achieved_error"] = {
-            "step": s.steps, "rows": int(wa.shape[0] * wa.shape[1]),
-            "a_full_max_abs": float(np.abs(ga - wa).max()),
-            "a_full_rel_l2": float(np.linalg.norm(ga - wa) / np.linalg.norm(wa)),
-            "l_full_max_abs": float(np.abs(gl - wl).max()),
+            "step": s.steps, "rows": int(len(done) * s.nb),
+            "a_full_max_abs": float(np.abs(pa - wa).max()),
+            "a_full_rel_l2": float(np.linalg.norm(pa - wa) / np.linalg.norm(wa)),
+            "l_full_max_abs": float(np.abs(pl - wl).max()),
             "bars": {"a_max_abs": 2e-2, "a_rel_l2": 5e-3, "l_max_abs": 1e-4}}
     return out
 
@@ -191,9 +231,9 @@ REUSE_REPS = 16   # reuse steps per graph in the reuse-step latency leg
 
 
 def measured_peaks(dev):
-    """Peaks measured on this machine, outside any timed region: a device copy of
-    1 GiB (bytes read + written per second) and a 8192^3 bf16 GEMM
-    (torch.matmul, i.e. the vendor BLAS)."""
+    """A peak measured on this machine, outside any timed region: a device copy
+    of 1 GiB (bytes read + written per second).  Context only: the roofline
+    fractions are against the published peaks."""
     import torch
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n = (1 << 30) // 4
@@ -208,26 +248,12 @@ def measured_peaks(dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * 5 * n * 4 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
     del src, dst
-    m = 8192
-    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
-    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
-    c = torch.matmul(a, b)
-    torch.cuda.synchronize()
-    ev[0].record()
-    for _ in range(5):
-        c = torch.matmul(a, b)
-    ev[1].record()
-    torch.cuda.synchronize()
-    gemm_tf = 5 * 2 * m ** 3 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
-    del a, b, c
-    return {"copy_gbs": round(copy_gbs, 1), "gemm_bf16_tflops": round(gemm_tf, 1)}
+    return {"copy_gbs": round(copy_gbs, 1)}
 
 
 def with_measured(roof, peaks):
-    """The roofline block plus the achieved rate as a fraction of the
-    matching measured peak."""
-    ref = peaks["copy_gbs"] if roof["bound"] == "hbm" else peaks["gemm_bf16_tflops"]
-    return {**roof, "measured_peak": peaks, "frac_of_measured": round(roof["achieved"] / ref, 4)}
+    """The roofline block plus the measured copy rate (context)."""
+    return {**roof, "measured_peak": peaks}
 
 
 def probe(args, s, q, kps, vps):
@@ -404,18 +430,14 @@ def run_varlen(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # noqa: BLE001
-            threads = 1
+        cores = host_cores()
         heads = list(range(0, vb.h, 4))
         t0 = time.perf_counter()
         oracle.run_varlen(vb, heads=heads)
         dt = time.perf_counter() - t0
         frac = len(heads) / vb.h
-        out["cpu_baseline"] = {"value": s_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-                               "kind": "oracle",
+        out["cpu_baseline"] = {"value": s_bytes * frac / dt / 1e9, "unit": "GB/s",
+                               "cores": cores["blas_threads"], **cores, "kind": "oracle",
                                "sample": f"one step of the same batch on {len(heads)} of {vb.h} heads "
                                          f"(bytes scaled to those heads), NumPy float64, {dt:.1f} s"}
     print(json.dumps(out), flush=True)
@@ -534,11 +556,7 @@ def run_sparse(args, s, q, kps, vps):
     }
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # noqa: BLE001
-            threads = 1
+        cores = host_cores()
         g = s.hq // s.hkv
         t0 = time.perf_counter()
         done = 0
@@ -550,8 +568,8 @@ def run_sparse(args, s, q, kps, vps):
                 break
         dt = time.perf_counter() - t0
         frac = done / (s.B * s.hq)
-        out["cpu_baseline"] = {"value": sel_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-                               "kind": "oracle",
+        out["cpu_baseline"] = {"value": sel_bytes * frac / dt / 1e9, "unit": "GB/s",
+                               "cores": cores["blas_threads"], **cores, "kind": "oracle",
                                "sample": f"the selected-block pass of {done} of {s.B * s.hq} (sequence, head) pairs, "
                                          f"bytes scaled to those, NumPy float64, {dt:.1f} s"}
     print(json.dumps(out), flush=True)
@@ -637,17 +655,13 @@ def run_kl(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # noqa: BLE001
-            threads = 1
+        cores = host_cores()
         rows = 64
         t0 = time.perf_counter()
         oracle.kl_rows(oracle.to_f64(cur[:rows], "bf16"), oracle.to_f64(prev[:rows], "bf16"))
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": nbytes * rows / KL_ROWS / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-                               "kind": "oracle",
+        out["cpu_baseline"] = {"value": nbytes * rows / KL_ROWS / dt / 1e9, "unit": "GB/s",
+                               "cores": cores["blas_threads"], **cores, "kind": "oracle",
                                "sample": f"{rows} of {KL_ROWS} rows, NumPy float64, {dt:.2f} s"}
     print(json.dumps(out), flush=True)
 
@@ -657,7 +671,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50, help="timed block schedules")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2_llada")
+    ap.add_argument("--workload", default="c3_gqa_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured copy and GEMM peaks (kernel traces of the path alone)")
@@ -729,6 +743,8 @@ def main():
     for t in range(1, s.steps + 1):
         attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
         decisions.append(attn.decision.cpu().numpy().copy())
+        if attn.waits_given_up():
+            raise RuntimeError(f"step {t}: a prefix workgroup gave up waiting for its gate")
     final_out = (attn.a_full.cpu().double().numpy().copy(), attn.l_full.cpu().double().numpy().copy())
     work = [step_work(s, decisions[t]) for t in range(1, s.steps + 1)]
     blk_bytes = sum(w[0] for w in work)
@@ -794,6 +810,36 @@ def main():
     if not args.no_peaks:
         roof = with_measured(roof, measured_peaks(dev))
 
+    # in-block leg: the part every step computes (A_in/L_in over the block and
+    # the fused merge with the cached prefix part into A_full/L_full), alone,
+    # as ba_block_attn calls captured in one graph
+    t_last = s.steps
+    ib = {nm: torch.empty_like(attn.a_out) for nm in ("a_in", "a_full")}
+    ib.update({nm: torch.empty_like(attn.l_out) for nm in ("l_in", "l_full")})
+    n_ib = 16
+    igraph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(igraph, stream=side):
+            for _ in range(n_ib):
+                ba.ba_block_attn(q[t_last], k[t_last], v[t_last], a_cache=attn.a_out, l_cache=attn.l_out,
+                                 a_in=ib["a_in"], l_in=ib["l_in"], a_full=ib["a_full"], l_full=ib["l_full"],
+                                 scale=s.scale, stream=torch.cuda.current_stream())
+    stream.wait_stream(side)
+    igraph.replay()
+    ib_us = timed(lambda i: igraph.replay(), 4) * 1e3 / n_ib
+    ib_flops = 4 * s.d * s.nb * s.nb * s.B * s.hq
+    ib_bytes = (s.B * s.nb * s.hq * s.d * 2 + 2 * s.B * s.nb * s.hkv * s.d * 2
+                + 2 * s.B * s.nb * s.hq * (s.d + 1) * 4 + s.B * s.nb * s.hq * (s.d + 1) * 4)
+    inblock = {"kernel": "in-block attention with the fused merge (ba_block_attn, A_in/L_in and "
+                         "A_full/L_full written)",
+               "us": round(ib_us, 2), "algorithmic_flops": ib_flops, "algorithmic_bytes": ib_bytes,
+               "tflops": round(ib_flops / (ib_us * 1e-6) / 1e12, 2),
+               "frac_mfma_bf16": round(ib_flops / (ib_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "gbs": round(ib_bytes / (ib_us * 1e-6) / 1e9, 1),
+               "timing": f"{n_ib} calls in one graph, 4 replays, HIP events on the launching stream"}
+
     out = {
         "metric": METRIC,
         "value": round(blk_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -830,9 +876,11 @@ def main():
             "gbs": round(achieved, 1),
             "tflops": round(achieved_tf, 3),
         },
+        "inblock": inblock,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
+        progress("CPU baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(s, got=final_out if s.gate != "partial" else None)
     print(json.dumps(out), flush=True)
 

@@ -12,7 +12,6 @@ from .api import (  # noqa: F401
     BA_GATE_COUNT_CUM,
     BA_GATE_ROWS,
     ba_block_attn,
-    ba_debug_set_gate_spin_limit,
     ba_gated_split_attn,
     ba_gated_split_attn_gate_workspace,
     ba_kl_lock,

@@ -13,8 +13,7 @@ import os
 import torch  # noqa: F401  (must load the HIP runtime before libba.so)
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-# BA_LIB selects another build of the same C-ABI (e.g. a debug build).
-LIB_PATH = os.environ.get("BA_LIB") or os.path.join(PKG_DIR, "libba.so")
+LIB_PATH = os.path.join(PKG_DIR, "libba.so")
 
 BA_OK = 0
 STATUS_NAMES = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_DTYPE",
@@ -48,6 +47,7 @@ class GateDesc(ctypes.Structure):
         ("v_cur", ctypes.c_void_p), ("v_prev", ctypes.c_void_p), ("kv_stride", c_i64x3),
         ("upd_mask", ctypes.c_void_p), ("tau", ctypes.c_int32), ("gamma", ctypes.c_double),
         ("cache_valid", ctypes.c_int32), ("since_refresh", ctypes.c_void_p),
+        ("wait_polls", ctypes.c_int32), ("gave_up", ctypes.c_void_p),
     ]
 
 
@@ -94,7 +94,6 @@ EXPORTS = {
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.c_void_p, ctypes.c_void_p]),
-    "ba_debug_set_gate_spin_limit": (ctypes.c_int32, [ctypes.c_int32]),
     "ba_last_error": (ctypes.c_char_p, []),
     "ba_version": (ctypes.c_int32, []),
 }

@@ -19,7 +19,7 @@ from ._lib import (AttnDesc, GateDesc, BA_BF16, BA_F32, BA_GATE_COUNT, BA_GATE_C
 __all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge", "ba_split_attn",
            "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
            "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
-           "ba_debug_set_gate_spin_limit", "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn", "ba_kl_lock",
+           "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn", "ba_kl_lock",
            "ba_prefix_attn_rows", "BA_GATE_COUNT", "BA_GATE_COSINE", "BA_GATE_COUNT_CUM", "BA_GATE_ROWS"]
 
 
@@ -116,12 +116,6 @@ def _check_out(t, shape, dtype, name):
 
 def ba_version() -> int:
     return lib().ba_version()
-
-
-def ba_debug_set_gate_spin_limit(polls: int) -> int:
-    """Testing aid: polls a gated prefix workgroup of ba_gated_split_attn makes for its
-    gate before giving up (negative = default); returns the previous value."""
-    return int(lib().ba_debug_set_gate_spin_limit(int(polls)))
 
 
 def ba_prefix_attn_workspace(q, k, v, *, q_layout="bshd", kv_layout="bhsd", cu_q=None, cu_k=None,
@@ -263,8 +257,8 @@ def ba_lse_merge(a1, l1, a2, l2, a, l=None, stream=None):
 
 
 def _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau, gamma, cache_valid,
-               since_refresh=None):
-    _need_gpu(q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, since_refresh)
+               since_refresh=None, wait_polls=0, gave_up=None):
+    _need_gpu(q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, since_refresh, gave_up)
     if q_cur.shape != q_prev.shape or q_cur.stride() != q_prev.stride():
         raise ValueError("q_cur and q_prev must share shape and strides")
     g = GateDesc()
@@ -295,6 +289,10 @@ def _gate_desc(mode, q_cur, q_prev, k_cur, k_prev, v_cur, v_prev, upd_mask, tau,
     if since_refresh is not None:
         _check_out(since_refresh, (g.n_seq, g.n_blk), torch.uint8, "since_refresh")
     g.since_refresh = _ptr(since_refresh)
+    g.wait_polls = int(wait_polls)
+    if gave_up is not None:
+        _check_out(gave_up, (1,), torch.int32, "gave_up")
+    g.gave_up = _ptr(gave_up)
     return g
 
 
@@ -331,16 +329,19 @@ def ba_gated_split_attn_gate_workspace(mode, q_cur, q_prev, **kw) -> int:
 def ba_gated_split_attn(mode, q_prev, kp, vp, k, v, a_out, l_out, a_in, l_in, a_full, l_full=None,
                         workspace=None, *, q, decision, gate_workspace, k_prev=None, v_prev=None,
                         upd_mask=None, tau=0, gamma=0.0, cache_valid=True, m_count=None, cos=None,
-                        since_refresh=None, kv_layout="bhsd", scale=None, stream=None):
+                        since_refresh=None, kv_layout="bhsd", scale=None, wait_polls=0, gave_up=None,
+                        stream=None):
     """The reuse gate (q/k/v against q_prev/k_prev/v_prev; count or cosine mode) and the
     split attention it gates, as ba_reuse_gate followed by ba_split_attn with
     decision = (decision if cache_valid else None), in two launches.  Dense
     block tensors [B, Nb, H, d]; `gate_workspace` is sized by
-    ba_gated_split_attn_gate_workspace and zero-filled before its first use."""
+    ba_gated_split_attn_gate_workspace and zero-filled before its first use.
+    wait_polls bounds the prefix workgroups' wait for the gate (0 = default,
+    < 0 = give up at once); gave_up (int32 [1]) counts the waits that gave up."""
     count = mode in (BA_GATE_COUNT, BA_GATE_COUNT_CUM)
     g = _gate_desc(mode, q, q_prev, k if count else None, k_prev if count else None,
                    v if count else None, v_prev if count else None, upd_mask, tau, gamma, cache_valid,
-                   since_refresh)
+                   since_refresh, wait_polls, gave_up)
     _need_gpu(decision, gate_workspace, m_count, cos)
     _check_out(decision, (g.n_seq, g.hq), torch.uint8, "decision")
     _check_out(m_count, (g.n_seq,), torch.int32, "m_count")

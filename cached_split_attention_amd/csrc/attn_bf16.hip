@@ -580,7 +580,9 @@ __device__ __forceinline__ bool any_recompute(const AttnParams& p, const Item& i
 // answer is shared through LDS, so every wave takes the same path.
 // Returns 0: all heads of the workgroup are reused (nothing to do); 1: all
 // recompute (count mode with M_b >= tau, or a wait that gave up, counted in
-// ready[n_seq]); 2: the per-head decisions are written (cosine mode).
+// *gave_up; the launch then writes split partials, which the combine pass
+// applies only where the decision is 0); 2: the per-head decisions are
+// written (cosine mode).
 __device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
   __shared__ int s_r;
   if (threadIdx.x == 0) {
@@ -589,7 +591,7 @@ __device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
     const int r = gate::wait_ready(word, count ? gate::kCountReady : p.hq, p.spin_limit);
     int res;
     if (r < 0) {
-      atomicAdd(p.ready + p.n_seq, 1);
+      if (p.gave_up) atomicAdd(p.gave_up, 1);
       res = 1;
     } else if (count) {
       res = (r & (gate::kCountReady - 1)) < p.gate_tau ? 0 : 1;

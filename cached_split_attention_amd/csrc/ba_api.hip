@@ -7,7 +7,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <atomic>
 #include <string>
 
 #include "ba_internal.h"
@@ -16,12 +15,11 @@ namespace {
 
 thread_local std::string g_err;
 
-// Polls (each an agent-scope load and a short sleep, about a microsecond) a
-// prefix workgroup makes for the gate of its own launch before it gives up
-// and recomputes its heads; far above the gate's running time.  Tests lower
-// it through ba_debug_set_gate_spin_limit to exercise the give-up path.
+// Default polls (each an agent-scope load and a short sleep, about a
+// microsecond) a prefix workgroup makes for the gate of its own launch before
+// it gives up and computes its heads into the split workspace; far above the
+// gate's running time.  The gate descriptor's wait_polls overrides it.
 constexpr int kGateSpinLimit = 1 << 20;
-std::atomic<int> g_spin_limit{kGateSpinLimit};
 
 ba_status fail(ba_status st, const char* fmt, ...) {
   char buf[512];
@@ -170,8 +168,17 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
 // Workspace: [partial A f32 [splits][entries][d]][partial L f32 [splits][entries]].
 // Workspace of a split plan: partial A [splits][entries][d] f32, then
 // partial L [splits][entries] f32.
-size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp) {
-  if (pp.n_splits <= 1) return 0;
+// A gated fused step (bf16, valid cache, some prefix keys) always writes
+// split partials, even with one split, so that a prefix workgroup whose wait
+// for the gate gave up cannot overwrite a reused head's cache: the combine
+// pass decides.  (With no prefix keys the result, A = 0 and L = -inf, does not
+// depend on the decision.)
+bool partial_always(const ba_attn_desc* d, bool gated_fused) {
+  return gated_fused && d->dtype == BA_BF16 && d->max_k > 0;
+}
+
+size_t prefix_ws_bytes(const ba_attn_desc* d, const PrefixPlan& pp, bool gated_fused = false) {
+  if (pp.n_splits <= 1 && !partial_always(d, gated_fused)) return 0;
   const size_t entries = (size_t)d->n_seq * d->max_q * d->hq;
   return (size_t)pp.n_splits * entries * (d->d + 1) * sizeof(float);
 }
@@ -210,12 +217,6 @@ const char* ba_last_error(void) { return g_err.c_str(); }
 
 int32_t ba_version(void) { return (1 << 16) | 0; }
 
-int32_t ba_debug_set_gate_spin_limit(int32_t polls) {
-  const int prev = g_spin_limit.load();
-  g_spin_limit.store(polls < 0 ? kGateSpinLimit : polls);
-  return prev;
-}
-
 namespace {
 
 // Recomputing shares the split planner averages over for a gated fused step
@@ -242,7 +243,7 @@ size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   if (check_desc(desc, &sh) != BA_OK) return 0;
   size_t need = 0;
   for (int shares : {0, seq_shares(desc->n_seq), kMaxShares}) {
-    const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares));
+    const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares), shares > 0);
     if (b > need) need = b;
   }
   return need;
@@ -257,7 +258,7 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
                       size_t workspace_bytes, hipStream_t stream, ba::AttnParams* block = nullptr,
                       const ba_attn_desc* block_desc = nullptr, const ba::GateParams* gate = nullptr,
                       const int32_t* kblocks = nullptr, int n_kblocks = -1, const int32_t* cu_rows = nullptr,
-                      const int32_t* rows = nullptr) {
+                      const int32_t* rows = nullptr, bool dry_run = false) {
   AttnShape sh;
   ba_status st = check_desc(desc, &sh);
   if (st != BA_OK) return st;
@@ -269,7 +270,10 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
   const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 0 : gate_shares(gate, desc));
-  const size_t need = prefix_ws_bytes(desc, pp);
+  // a gated fused step's prefix workgroups may give up waiting for the gate:
+  // their results then go through the split workspace (see prefix_ws_bytes)
+  const bool always_partial = partial_always(desc, gate != nullptr && desc->decision != nullptr);
+  const size_t need = prefix_ws_bytes(desc, pp, always_partial);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if ((int64_t)pp.n_splits * pp.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
@@ -290,7 +294,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
   if (gate) {
     p.ready = gate->ready;
     p.ready_stride = gate->ready_stride;
-    p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    p.spin_limit = gate->spin_limit;
+    p.gave_up = gate->gave_up;
     p.gate_mode = gate->mode;
     p.gate_tau = gate->tau;
   }
@@ -302,8 +307,9 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     if ((int64_t)block->row_tiles * block_desc->n_seq * block_desc->hkv > 0x7fffff00LL)
       return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
   }
+  if (dry_run) return BA_OK;
   hipError_t err;
-  if (desc->dtype == BA_F32 || pp.n_splits == 1) {
+  if (desc->dtype == BA_F32 || (pp.n_splits == 1 && !always_partial)) {
     p.mode = ba::kPrefixFinal;
   } else {
     const size_t entries = (size_t)desc->n_seq * desc->max_q * desc->hq;
@@ -410,7 +416,8 @@ namespace {
 // the same launch), then the combine-and-merge pass.
 ba_status split_impl(const ba_attn_desc* prefix, const ba_attn_desc* block, float* a_out, float* l_out,
                      float* a_in, float* l_in, float* a_full, float* l_full, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream, const ba::GateParams* gate) {
+                     size_t workspace_bytes, hipStream_t stream, const ba::GateParams* gate,
+                     bool dry_run = false) {
   AttnShape sp, sb;
   ba_status st = check_desc(prefix, &sp);
   if (st != BA_OK) return st;
@@ -430,7 +437,7 @@ ba_status split_impl(const ba_attn_desc* prefix, const ba_attn_desc* block, floa
   pb.a = a_in;
   pb.l = l_in;
   return prefix_impl(prefix, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream, &pb,
-                     block, gate);
+                     block, gate, nullptr, -1, nullptr, nullptr, dry_run);
 }
 
 }  // namespace
@@ -557,6 +564,8 @@ ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint
   p.cache_valid = g->cache_valid ? 1 : 0;
   p.since = g->mode == BA_GATE_COUNT_CUM ? g->since_refresh : nullptr;
   p.pos_per_wg = 1;
+  p.spin_limit = g->wait_polls == 0 ? kGateSpinLimit : (g->wait_polls < 0 ? 0 : g->wait_polls);
+  p.gave_up = g->gave_up;
   p.chunks = count ? 1 : ba::gate_cos_chunks(g->n_blk, g->d);
   bool v16 = (g->d * p.esize) % 16 == 0;
   const void* ptrs[6] = {g->q_cur, g->q_prev, g->k_cur, g->k_prev, g->v_cur, g->v_prev};
@@ -577,9 +586,9 @@ ba_status gate_params(const ba_gate_desc* g, int32_t* m_count, double* cos, uint
 }
 
 // A fused call's gate workspace: the gate's own, then kReadyCopies copies of
-// the per-sequence ready words (each copy n_seq + 1 ints rounded up to a
-// 128-byte line; int n_seq of copy 0 counts waits that gave up).
-size_t ready_stride_ints(const ba_gate_desc* g) { return ((size_t)g->n_seq + 1 + 31) & ~(size_t)31; }
+// the per-sequence ready words (each copy n_seq ints rounded up to a
+// 128-byte line).
+size_t ready_stride_ints(const ba_gate_desc* g) { return ((size_t)g->n_seq + 31) & ~(size_t)31; }
 
 size_t fused_gate_ws_bytes(const ba_gate_desc* g) {
   const size_t own = ba::gate_workspace_bytes(g->mode, g->n_seq, g->hq, g->n_blk, g->d);
@@ -627,7 +636,11 @@ ba_status ba_gated_split_attn(const ba_gate_desc* gate, int32_t* m_count, double
   ba_attn_desc pd = *prefix;
   pd.decision = gate->cache_valid ? decision : nullptr;
   if (prefix->dtype == BA_F32 || prefix->n_seq == 0 || prefix->max_q == 0) {
-    // no fused launch for the float32 kernel: the gate, then the split pass
+    // no fused launch for the float32 kernel: the gate, then the split pass,
+    // whose arguments are all checked before the gate is enqueued
+    st = split_impl(&pd, block, a_out, l_out, a_in, l_in, a_full, l_full, workspace, workspace_bytes, stream,
+                    nullptr, /*dry_run=*/true);
+    if (st != BA_OK) return st;
     if (prefix->n_seq > 0) {
       const hipError_t e = ba::launch_gate(gp, stream);
       if (e != hipSuccess) return hip_status(e, "reuse gate");

@@ -46,11 +46,14 @@ struct AttnParams {
   // from which it decides itself against gate_tau; cosine mode: all hq
   // decisions written), polling copy (workgroup % kReadyCopies) of the
   // ready words at most spin_limit times; a wait that gives up counts itself
-  // in ready[n_seq] and recomputes its heads.  The combine pass after such a
-  // launch zeroes ready[0 .. n_seq) of every copy.
+  // in *gave_up (if set) and computes its heads into the split workspace
+  // (mode kPrefixPartial), where the combine pass applies the decisions.
+  // The combine pass after such a launch zeroes ready[0 .. n_seq) of every
+  // copy.
   int32_t* ready;
   int ready_stride;
   int spin_limit;
+  int32_t* gave_up;
   int gate_mode;
   int gate_tau;
   // Key-block list mode (dense prefix only): (sequence, KV head) attends over
@@ -130,6 +133,9 @@ struct GateParams {
   int ready_stride;    // ints between copies
   uint8_t* since;      // cumulative count mode: positions updated since the last refresh
   int pos_per_wg;      // count modes: block positions per workgroup (1 .. 32)
+  // fused step only: the waiting prefix workgroups' poll bound and give-up count
+  int spin_limit;
+  int32_t* gave_up;
 };
 constexpr int kReadyCopies = 4;
 constexpr int kMaxGatePositions = 32;   // count-gate positions per workgroup (one mask bit each)

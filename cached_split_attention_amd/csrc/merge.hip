@@ -18,8 +18,22 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeParams p) {
   const int rpb = 256 / tpr;
   const int64_t row = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
   const int t = threadIdx.x % tpr;
-  if (row >= p.rows) return;
-  const float l1 = p.l1[row], l2 = p.l2[row];
+  // Threads past the last row (or past rpb * tpr) only join the barrier.
+  const bool valid = threadIdx.x < rpb * tpr && row < p.rows;
+  float l1 = -INFINITY, l2 = -INFINITY;
+  f32x4 x1 = {0.0f, 0.0f, 0.0f, 0.0f}, x2 = x1;
+  if (valid) {
+    l1 = p.l1[row];
+    l2 = p.l2[row];
+    x1 = *reinterpret_cast<const f32x4*>(p.a1 + row * p.d + 4 * t);
+    x2 = *reinterpret_cast<const f32x4*>(p.a2 + row * p.d + 4 * t);
+  }
+  // Every read of the workgroup's rows completes before any write: a row's
+  // d/4 threads can span two waves (d/4 need not divide 64), and in-place
+  // use (a == a1 or a2, l == l1 or l2) must not let one wave's store of L
+  // reach another wave's load of it.
+  __syncthreads();
+  if (!valid) return;
   const float m = fmaxf(l1, l2);
   float w1 = 0.0f, w2 = 0.0f, rden = 0.0f, lf = -INFINITY;
   if (m != -INFINITY) {
@@ -29,10 +43,6 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeParams p) {
     rden = 1.0f / den;
     lf = m + __logf(den);
   }
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(p.a1 + row * p.d + 4 * t);
-  const f32x4 x2 = *reinterpret_cast<const f32x4*>(p.a2 + row * p.d + 4 * t);
-  // All reads of this row happen before any write, so a == a1 / a == a2 is safe.
-  __builtin_amdgcn_wave_barrier();
   const f32x4 y = (w1 * rden) * x1 + (w2 * rden) * x2;
   *reinterpret_cast<f32x4*>(p.a + row * p.d + 4 * t) = y;
   if (p.l && t == 0) p.l[row] = lf;

@@ -66,6 +66,10 @@ class CachedBlockAttention:
         self.decision = torch.zeros(self.B, hq, device=dev, dtype=torch.uint8)
         self.m_count = torch.zeros(self.B, device=dev, dtype=torch.int32)
         self.cos = torch.zeros(self.B, hq, device=dev, dtype=torch.float64)
+        # prefix workgroups whose bounded wait for their gate gave up (the
+        # result does not depend on it; a nonzero count means the gate ran
+        # far slower than expected)
+        self.gave_up = torch.zeros(1, device=dev, dtype=torch.int32)
         if self.mode == BA_GATE_COUNT_CUM:
             self.since_refresh = torch.zeros(self.B, nb, device=dev, dtype=torch.uint8)
         if self.mode == BA_GATE_ROWS:
@@ -117,9 +121,14 @@ class CachedBlockAttention:
                             cache_valid=self.cache_valid, m_count=self.m_count if count else None,
                             cos=None if count else self.cos,
                             since_refresh=getattr(self, "since_refresh", None), kv_layout=self.kv_layout,
-                            scale=self.scale, stream=main)
+                            scale=self.scale, gave_up=self.gave_up, stream=main)
         self.cache_valid = True
         return self.a_full, self.l_full
+
+    def waits_given_up(self) -> int:
+        """Prefix workgroups that gave up waiting for their gate so far (reads
+        the device counter; synchronises)."""
+        return int(self.gave_up.item())
 
     def _partial_step(self, q, k, v, q_prev, stream):
         # rows whose Q is unchanged keep their cached prefix part (all rows

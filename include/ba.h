@@ -267,6 +267,14 @@ typedef struct ba_gate_desc {
   double gamma;
   int32_t cache_valid;      /* 0 = no cache yet (first step of a block)        */
   uint8_t* since_refresh;   /* BA_GATE_COUNT_CUM state; NULL in other modes    */
+  /* ba_gated_split_attn only (ignored by ba_reuse_gate):                     */
+  int32_t wait_polls;       /* polls of a prefix workgroup's bounded wait for
+                               the gate: 0 = the default (about a second),
+                               > 0 = that many, < 0 = none (every gated prefix
+                               workgroup gives up at once; for failure-
+                               handling tests)                                 */
+  int32_t* gave_up;         /* optional device int32: one is added per prefix
+                               workgroup that gave up waiting                  */
 } ba_gate_desc;
 
 /*
@@ -301,10 +309,16 @@ ba_status ba_reuse_gate(const ba_gate_desc* g, int32_t* m_count, double* cos,
  *     dtype and n_blk must equal prefix->n_seq, hq, dtype and max_q.
  *   gate_workspace: ba_gated_split_attn_gate_workspace(gate) bytes, zero-
  *     filled before first use; every call that returns BA_OK leaves it zero
- *     again, except that prefix workgroups that gave up waiting for the gate
- *     (after about a second; they then recompute their heads, which is exact
- *     attention) are counted in one of its int32 words.  A call whose launch
- *     fails leaves it undefined: zero it again.
+ *     again.  A call whose launch fails leaves it undefined: zero it again.
+ *   A prefix workgroup whose wait for the gate runs out (gate->wait_polls;
+ *     by default after about a second, far beyond the gate's running time)
+ *     computes its heads into the split workspace instead, and the combine
+ *     pass, which runs after the gate has finished, applies the gate's
+ *     decisions to them: the outputs do not depend on whether a wait gave
+ *     up.  Such workgroups are counted in *gate->gave_up when it is given.
+ *   With a valid cache (bf16) the prefix part always goes through the split
+ *     workspace, even with a single key split, so `workspace` is required;
+ *     ba_prefix_attn_workspace(prefix) covers it.
  *   prefix->decision must be NULL; everything else as for ba_split_attn.
  * The float32 dtype runs the two calls in sequence (no fused launch).
  */
@@ -357,16 +371,6 @@ ba_status ba_varlen_pack(int32_t n_branch, const int32_t* block_sizes_host,
                          int32_t* total, int32_t dtype, int32_t h, int32_t d,
                          const void* q_src, const int64_t q_src_stride[2], void* q_packed,
                          hipStream_t stream);
-
-/*
- * Testing aid for the callers' failure-handling tests, not for production
- * use: sets how many times a prefix workgroup of ba_gated_split_attn polls
- * for its gate before giving up (negative restores the default, about a
- * second); returns the previous value.  Applies to calls made after it, from
- * any thread.  With 0, every gated prefix workgroup gives up at once,
- * recomputes its heads and is counted in the gate workspace.
- */
-int32_t ba_debug_set_gate_spin_limit(int32_t polls);
 
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* ba_last_error(void);

@@ -114,6 +114,54 @@ def test_prefix_workspace_covers_gated_split(lib):
     assert need >= 16 * (8 * 16 * 8) * 129 * 4
 
 
+def test_prefix_workspace_covers_gated_single_split(lib):
+    # A 64-key prefix needs one key split, so an ungated pass needs no
+    # workspace; a gated fused step still writes its prefix part as split
+    # partials (a prefix workgroup that gave up waiting for the gate must
+    # not overwrite a reused head's cache), and the query covers that.
+    d = good_desc()
+    d.max_k = 64
+    for i, s in enumerate((2 * 64 * 128, 128, 64 * 128)):
+        d.k_stride[i] = s
+        d.v_stride[i] = s
+    need = lib.ba_prefix_attn_workspace(ctypes.byref(d))
+    assert need >= (32 * 4) * 129 * 4
+
+
+def f32_pair():
+    """A float32 prefix / block descriptor pair for one fused step (4 heads,
+    32 block rows) and its matching count gate."""
+    p = good_desc()
+    p.dtype = 1
+    for i, s in enumerate((32 * 4 * 128, 4 * 128, 128)):
+        p.q_stride[i] = s
+    b = good_desc()
+    b.dtype, b.max_k = 1, 32
+    for i, s in enumerate((32 * 2 * 128, 2 * 128, 128)):
+        b.k_stride[i] = s
+        b.v_stride[i] = s
+    g = good_gate()
+    g.dtype, g.n_seq, g.hq = 1, 1, 4
+    return p, b, g
+
+
+def test_fused_f32_validates_before_the_gate(lib):
+    # The float32 fused step runs the gate and then the split pass as two
+    # launches; a bad prefix descriptor must be rejected before the gate is
+    # enqueued (with no GPU here, an enqueued gate would report a HIP error
+    # instead of the validation failure).
+    p, b, g = f32_pair()
+    p.d = 96
+    gws = lib.ba_gated_split_attn_gate_workspace(ctypes.byref(g))
+    st, msg = status_of(lib, lib.ba_gated_split_attn, ctypes.byref(g), FAKE, None, FAKE, FAKE, gws,
+                        ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 4 and "head dim" in msg, (st, msg)
+    p, b, g = f32_pair()
+    st, msg = status_of(lib, lib.ba_gated_split_attn, ctypes.byref(g), FAKE, None, FAKE, FAKE, gws,
+                        ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 1 and "a_in" in msg, (st, msg)
+
+
 def test_prefix_empty_is_ok_without_launch(lib):
     d = good_desc()
     d.n_seq = 0

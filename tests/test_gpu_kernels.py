@@ -32,7 +32,7 @@ def f64(x, dtype):
 # ba_lse_merge
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 132, 512, 1024])
 def test_lse_merge(d):
     r = np.random.default_rng(40 + d)
     rows = 1237
@@ -55,11 +55,18 @@ def test_lse_merge(d):
     assert np.array_equal(np.isneginf(got_l), np.isneginf(wl))
     fin = ~np.isneginf(wl)
     np.testing.assert_allclose(got_l[fin], wl[fin], atol=2e-5 * max(1, np.abs(wl[fin]).max() / 100), rtol=0)
-    # in place into the first operand
-    x1, y1 = dev_f32(a1), dev_f32(l1)
-    ba.ba_lse_merge(x1, y1, dev_f32(a2), dev_f32(l2), x1, y1)
-    torch.cuda.synchronize()
-    np.testing.assert_allclose(host(x1), wa, atol=2e-6, rtol=0)
+    # in place into the first operand, and into the second: A and L (a
+    # row's threads span two waves whenever d/4 does not divide 64)
+    for into in (1, 2):
+        x1, y1, x2, y2 = dev_f32(a1), dev_f32(l1), dev_f32(a2), dev_f32(l2)
+        xa, xl = (x1, y1) if into == 1 else (x2, y2)
+        ba.ba_lse_merge(x1, y1, x2, y2, xa, xl)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(host(xa), wa, atol=2e-6, rtol=0, err_msg=f"in place into operand {into}")
+        got_l = host(xl)
+        assert np.array_equal(np.isneginf(got_l), np.isneginf(wl)), f"in place into operand {into}"
+        np.testing.assert_allclose(got_l[fin], wl[fin], atol=2e-5 * max(1, np.abs(wl[fin]).max() / 100), rtol=0,
+                                   err_msg=f"in place L into operand {into}")
 
 
 # ----------------------------------------------------------------------------
@@ -773,20 +780,23 @@ def test_gated_split_attn_finer_split(mode):
     assert not host(gws).view(np.int32).any(), "gate workspace not left zero"
 
 
+@pytest.mark.parametrize("lp", [512, 64])
 @pytest.mark.parametrize("mode", ["count", "cosine"])
-def test_gated_split_attn_gives_up(mode):
+def test_gated_split_attn_gives_up(mode, lp):
     # The prefix workgroups' bounded wait for the gate, forced to give up at
-    # once from the host (spin limit 0): every gated prefix workgroup counts
-    # itself in the gate workspace and recomputes its heads.  With split
-    # partials the combine pass still applies the gate's decisions, so the
-    # outputs equal those of the gate followed by the split pass.
-    B, hq, hkv, d, lp, nb = 2, 8, 8, 128, 512, 32
+    # once from the host (wait_polls < 0): every gated prefix workgroup is
+    # counted and computes its heads into the split workspace, and the
+    # combine pass, which runs after the gate, applies the gate's decisions.
+    # So the outputs equal those of the gate followed by the split pass, with
+    # several key splits (lp 512) and with one (lp 64), and reused heads keep
+    # their cache bit for bit.
+    B, hq, hkv, d, nb = 2, 8, 8, 128, 32
     s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=93)
     rows = B * nb
     q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
     kp, vp = dev_in(s.kp, "bf16"), dev_in(s.vp, "bf16")
     nws = ba.ba_prefix_attn_workspace(q, kp, vp)
-    assert nws > 0, "shape must use split partials"
+    assert nws > 0, "a gated fused step always has a split workspace"
     if mode == "count":
         q_prev, k_prev, v_prev = q.clone(), k.clone(), v.clone()
         for pos in range(6):
@@ -799,8 +809,10 @@ def test_gated_split_attn_gives_up(mode):
         q_prev[0] = q[0]                 # sequence 0 reused (cosine 1)
         bmode, gkw, gate_kw = ba.BA_GATE_COSINE, {}, dict(gamma=0.99)
     r = np.random.default_rng(7)
-    cache_a = torch.from_numpy(r.standard_normal((rows, hq, d)).astype(np.float32)).to(DEV)
-    cache_l = torch.from_numpy(r.standard_normal((rows, hq)).astype(np.float32)).to(DEV)
+    cache_a_h = r.standard_normal((rows, hq, d)).astype(np.float32)
+    cache_l_h = r.standard_normal((rows, hq)).astype(np.float32)
+    cache_a = torch.from_numpy(cache_a_h).to(DEV)
+    cache_l = torch.from_numpy(cache_l_h).to(DEV)
     outs = {}
     for which in ("ref", "fused"):
         o = dict(a_out=cache_a.clone(), l_out=cache_l.clone(), a_in=torch.empty(rows, hq, d, device=DEV),
@@ -818,30 +830,36 @@ def test_gated_split_attn_gives_up(mode):
         else:
             gws = torch.zeros(ba.ba_gated_split_attn_gate_workspace(bmode, q, q_prev, **gkw), device=DEV,
                               dtype=torch.uint8)
-            prev = ba.ba_debug_set_gate_spin_limit(0)
-            try:
-                ba.ba_gated_split_attn(bmode, q_prev, kp, vp, k, v, o["a_out"], o["l_out"], o["a_in"], o["l_in"],
-                                       o["a_full"], o["l_full"], o["ws"], q=q, decision=o["dec"], gate_workspace=gws,
-                                       k_prev=k_prev, v_prev=v_prev, m_count=o["m"] if count else None,
-                                       cos=None if count else o["cos"], **gate_kw)
-                torch.cuda.synchronize()
-            finally:
-                ba.ba_debug_set_gate_spin_limit(prev)
-            o["gws"] = gws
+            gave_up = torch.zeros(1, device=DEV, dtype=torch.int32)
+            ba.ba_gated_split_attn(bmode, q_prev, kp, vp, k, v, o["a_out"], o["l_out"], o["a_in"], o["l_in"],
+                                   o["a_full"], o["l_full"], o["ws"], q=q, decision=o["dec"], gate_workspace=gws,
+                                   k_prev=k_prev, v_prev=v_prev, m_count=o["m"] if count else None,
+                                   cos=None if count else o["cos"], wait_polls=-1, gave_up=gave_up, **gate_kw)
+            o["gws"], o["gave_up"] = gws, gave_up
         torch.cuda.synchronize()
         outs[which] = o
     ref, fused = outs["ref"], outs["fused"]
     dv = host(ref["dec"])
     assert dv[0].all() and not dv[1].any(), "schedule should reuse sequence 0 and recompute sequence 1"
     assert torch.equal(fused["dec"], ref["dec"])
-    gave_up = int(host(fused["gws"]).view(np.int32).sum())
-    assert gave_up > 0, "no prefix workgroup was counted as giving up"
+    assert int(fused["gave_up"].item()) > 0, "no prefix workgroup was counted as giving up"
+    assert not host(fused["gws"]).view(np.int32).any(), "gate workspace not left zero"
     for nm in ("a_in", "l_in", "a_full", "l_full"):
         assert torch.allclose(fused[nm], ref[nm], rtol=1e-6, atol=1e-6), nm
     # recomputed heads' A_out is fresh either way; reused heads keep the cache
     for nm in ("a_out", "l_out"):
         assert torch.equal(fused[nm][nb:], ref[nm][nb:]), nm
         assert torch.equal(fused[nm][:nb], ref[nm][:nb]), nm
+    np.testing.assert_array_equal(host(fused["a_out"])[:nb], cache_a_h[:nb])
+    np.testing.assert_array_equal(host(fused["l_out"])[:nb], cache_l_h[:nb])
+    # and against the oracle: sequence 1 recomputed with the current Q,
+    # sequence 0 merged with its (arbitrary) cache
+    wa_in, wl_in = _oracle_block(s)
+    wa_out, wl_out = _oracle_prefix(s)
+    wa_out[:nb], wl_out[:nb] = cache_a_h[:nb], cache_l_h[:nb]
+    wa, wl = oracle.merge(wa_out, wl_out, wa_in, wl_in)
+    check_a(host(fused["a_full"]), wa, "A_full against the oracle")
+    check_l(host(fused["l_full"]), wl, "L_full against the oracle")
 
 
 SPARSE_SHAPES = [

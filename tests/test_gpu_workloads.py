@@ -52,7 +52,37 @@ def _sampled_rows(sched, t, gates_hist, last, rows, got_a, got_l):
         check_l(got_l[r, h][None], lf, f"L_full step {t} (b{b} h{h} i{i})")
 
 
-def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=False, seed=0, **overrides):
+def _check_whole_heads(sched, t, pairs, last, attn, cache, name):
+    """Every row of the (b, h) pairs at step t against the oracle: A_in/L_in
+    over the block, the cached A_out/L_out (prefix part with the Q of the step
+    that last refreshed the head), and their merge A_full/L_full."""
+    nb, hq, d = sched.nb, sched.hq, sched.d
+    ga_in, gl_in = host(attn.a_in).reshape(-1, hq, d), host(attn.l_in).reshape(-1, hq)
+    ga_out, gl_out = host(attn.a_out).reshape(-1, hq, d), host(attn.l_out).reshape(-1, hq)
+    ga_f, gl_f = host(attn.a_full).reshape(-1, hq, d), host(attn.l_full).reshape(-1, hq)
+    for b, h in pairs:
+        tr = int(last[t][b, h])
+        key = (tr, b, h)
+        if key not in cache:
+            cache[key] = oracle.prefix_rows(sched, tr, b, h)
+        ao, lo = cache[key]
+        ai, li = oracle.block_rows(sched, t, b, h)
+        af, lf = oracle.merge(ao, lo, ai, li)
+        rs = slice(b * nb, (b + 1) * nb)
+        what = f"[{name}] step {t} b{b} h{h} (refreshed at step {tr}), all {nb} rows"
+        check_a(ga_in[rs, h], ai, "A_in " + what)
+        check_l(gl_in[rs, h], li, "L_in " + what)
+        check_a(ga_out[rs, h], ao, "A_out " + what)
+        check_l(gl_out[rs, h], lo, "L_out " + what)
+        check_a(ga_f[rs, h], af, "A_full " + what)
+        check_l(gl_f[rs, h], lf, "L_full " + what)
+    say(f"[{name}] step {t}: every row of {len(pairs)} (sequence, head) pairs checked")
+
+
+def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=False, seed=0, whole=None,
+                          **overrides):
+    """whole(sched, gates) -> {step: [(b, h), ...]}: (sequence, head) pairs
+    whose every row is checked at that step, besides the sampled rows."""
     sched = preset(name, **overrides)
     say(f"[{name}] B={sched.B} Hq={sched.hq} Hkv={sched.hkv} d={sched.d} Lp={sched.lp} Nb={sched.nb} "
         f"steps={sched.steps} gate={sched.gate}")
@@ -66,6 +96,8 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
     attn = ba.CachedBlockAttention(kp, vp, nb=sched.nb, hq=sched.hq, gate=sched.gate, tau=sched.tau,
                                    gamma=sched.gamma, scale=sched.scale)
     ref_full = oracle.run_block(sched) if full_rows else None
+    whole_at = whole(sched, gates) if whole is not None else {}
+    prefix_cache = {}
     rng = np.random.default_rng(seed)
     outs = []
     if use_graph:
@@ -85,7 +117,10 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
         assert np.array_equal(dec, gates[t]["decision"]), f"[{name}] step {t}: decisions differ"
         if sched.gate in ("count", "count_cum"):
             assert np.array_equal(attn.m_count.cpu().numpy(), gates[t]["m"]), f"[{name}] step {t}: M differs"
+        assert attn.waits_given_up() == 0, f"[{name}] step {t}: a prefix workgroup gave up waiting for its gate"
         recomputes += int((dec == 0).sum())
+        if t in whole_at:
+            _check_whole_heads(sched, t, whole_at[t], last, attn, prefix_cache, name)
         ga, gl = host(af), host(lf)
         if full_rows:
             check_a(ga, ref_full[t]["a_full"], f"[{name}] A_full step {t}")
@@ -114,13 +149,42 @@ def test_workload_llada():
     _run_schedule_checked("c2_llada", full_rows=True, use_graph=True)
 
 
+def _gqa_whole(sched, gates):
+    # A sequence with a gated recompute: every head and row of it at the
+    # first step, at its gated recompute, at the next step (which reuses it)
+    # and at the last step; plus one (sequence, KV head) group of another
+    # sequence (its 4 query heads) at the gated recompute step.
+    rec = [(t, b) for t in range(2, sched.steps + 1) for b in range(sched.B)
+           if (gates[t]["decision"][b] == 0).all()]
+    assert rec, "the schedule has no gated recompute"
+    t_r, b = rec[0]
+    t_u = next(t for t in range(t_r + 1, sched.steps + 1) if gates[t]["decision"][b].all())
+    g = sched.hq // sched.hkv
+    b2 = (b + 1) % sched.B
+    heads = [(b, h) for h in range(sched.hq)]
+    out = {1: heads, t_r: heads + [(b2, h) for h in range(2 * g, 3 * g)], t_u: heads, sched.steps: heads}
+    return out
+
+
 def test_workload_gqa_long_context():
-    sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=6, use_graph=False, seed=3)
+    sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=6, use_graph=False, seed=3, whole=_gqa_whole)
     assert rec > sched.B * sched.hq  # gated recomputes beyond the first step
 
 
+def _video_whole(sched, gates):
+    # Every row (all 13 row tiles of the 1560-row block, its 24-row tail) of
+    # two heads: one the similarity gate reuses and one it recomputes at the
+    # first step that has both, checked there and at the last step.
+    t1 = next(t for t in range(2, sched.steps + 1)
+              if gates[t]["decision"][0].any() and not gates[t]["decision"][0].all())
+    dec = gates[t1]["decision"][0]
+    h_reuse, h_rec = int(np.flatnonzero(dec == 1)[0]), int(np.flatnonzero(dec == 0)[-1])
+    pairs = [(0, h_reuse), (0, h_rec)]
+    return {t1: pairs, sched.steps: pairs}
+
+
 def test_workload_video():
-    sched, rec = _run_schedule_checked("c4_video", rows_per_step=6, use_graph=False, seed=4)
+    sched, rec = _run_schedule_checked("c4_video", rows_per_step=6, use_graph=False, seed=4, whole=_video_whole)
     assert sched.B * sched.hq < rec < sched.steps * sched.B * sched.hq  # some heads reuse
 
 
@@ -194,7 +258,7 @@ def test_workload_varlen_branches():
     vb = preset("c5_varlen")
     say(f"[c5_varlen] block sizes {vb.block_sizes.tolist()} prefixes {vb.prefix_lens.tolist()} "
         f"H={vb.h} d={vb.d} locked={int(vb.locked.sum())}")
-    heads = [0, 7, 19, 31]
+    heads = list(range(vb.h))
     ref = oracle.run_varlen(vb, heads=heads)
     dev = "cuda"
     n = int(vb.block_sizes.sum())
@@ -234,7 +298,7 @@ def test_workload_varlen_branches():
         check_l(glo[:, h], ref["l_out"][:, h], f"[c5_varlen] L_out head {h}")
         check_a(ga[:, h], ref["a_full"][:, h], f"[c5_varlen] A_full head {h}")
         check_l(gl[:, h], ref["l_full"][:, h], f"[c5_varlen] L_full head {h}")
-    say(f"[c5_varlen] {tot} packed rows checked on heads {heads}")
+    say(f"[c5_varlen] {tot} packed rows checked on all {vb.h} heads")
     # the same step through the one-launch split attention (prefix and
     # in-block parts together, then combine and merge)
     outs = {nm: torch.empty(n, vb.h, vb.d, device=dev) for nm in ("a_out", "a_in", "a_full")}
@@ -249,7 +313,7 @@ def test_workload_varlen_branches():
             check_a(host(outs[nm])[:tot, h], ref[nm][:, h], f"[c5_varlen split] {nm} head {h}")
         for nm in ("l_out", "l_in", "l_full"):
             check_l(host(outs[nm])[:tot, h], ref[nm][:, h], f"[c5_varlen split] {nm} head {h}")
-    say(f"[c5_varlen] split attention checked on heads {heads}")
+    say(f"[c5_varlen] split attention checked on all {vb.h} heads")
 
 
 @pytest.mark.parametrize("gate", ["count_cum", "partial"])
