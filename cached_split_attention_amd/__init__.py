@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     ba_lse_merge,
     ba_prefix_attn,
     ba_prefix_attn_merge,
+    ba_prefix_attn_noalloc,
     ba_prefix_attn_rows,
     ba_prefix_attn_workspace,
     ba_reuse_gate,

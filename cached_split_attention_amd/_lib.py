@@ -19,6 +19,7 @@ BA_OK = 0
 STATUS_NAMES = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_DTYPE",
                 4: "BA_ERR_UNSUPPORTED", 5: "BA_ERR_WORKSPACE", 6: "BA_ERR_HIP"}
 BA_BF16, BA_F32 = 0, 1
+BA_NOALLOC_SCRATCH_BYTES = 64 << 20   # as in ba.h
 BA_GATE_COUNT, BA_GATE_COSINE, BA_GATE_COUNT_CUM, BA_GATE_ROWS = 0, 1, 2, 3
 
 c_i64x3 = ctypes.c_int64 * 3
@@ -55,6 +56,8 @@ EXPORTS = {
     "ba_prefix_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc)]),
     "ba_prefix_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "ba_prefix_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
     "ba_prefix_attn_rows": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),

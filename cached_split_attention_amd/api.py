@@ -20,7 +20,7 @@ __all__ = ["ba_prefix_attn_workspace", "ba_prefix_attn", "ba_prefix_attn_merge",
            "ba_block_attn", "ba_lse_merge", "ba_reuse_gate_workspace", "ba_reuse_gate",
            "ba_gated_split_attn_gate_workspace", "ba_gated_split_attn", "ba_varlen_pack", "ba_version",
            "ba_sparse_prefix_attn_workspace", "ba_sparse_prefix_attn", "ba_kl_lock",
-           "ba_prefix_attn_rows", "BA_GATE_COUNT", "BA_GATE_COSINE", "BA_GATE_COUNT_CUM", "BA_GATE_ROWS"]
+           "ba_prefix_attn_rows", "ba_prefix_attn_noalloc", "BA_GATE_COUNT", "BA_GATE_COSINE", "BA_GATE_COUNT_CUM", "BA_GATE_ROWS"]
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -137,6 +137,17 @@ def ba_prefix_attn(q, k, v, a_out, l_out, workspace=None, *, q_layout="bshd", kv
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().ba_prefix_attn(ctypes.byref(desc), _ptr(a_out), _ptr(l_out), _ptr(workspace), nbytes,
                                _stream(stream)))
+
+
+def ba_prefix_attn_noalloc(q, k, v, a_out, l_out, *, q_layout="bshd", kv_layout="bhsd", cu_q=None, cu_k=None,
+                           max_q=None, max_k=None, decision=None, scale=None, stream=None):
+    """ba_prefix_attn with its split partials in the library's static per-GPU scratch
+    (no workspace, no allocation; calls overlapping on one GPU race)."""
+    desc, rows = _desc(q, k, v, q_layout=q_layout, kv_layout=kv_layout, cu_q=cu_q, cu_k=cu_k,
+                       max_q=max_q, max_k=max_k, scale=scale, decision=decision)
+    _check_out(a_out, (rows, desc.hq, desc.d), torch.float32, "a_out")
+    _check_out(l_out, (rows, desc.hq), torch.float32, "l_out")
+    check(lib().ba_prefix_attn_noalloc(ctypes.byref(desc), _ptr(a_out), _ptr(l_out), _stream(stream)))
 
 
 def ba_prefix_attn_rows(q, k, v, cu_rows, rows, a_out, l_out, workspace=None, *, kv_layout="bhsd", scale=None,

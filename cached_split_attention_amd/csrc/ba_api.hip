@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "ba_internal.h"
@@ -386,6 +387,64 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out, v
                          size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
   return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of ba_prefix_attn_noalloc: the split-KV partials of one call, in a
+// file-scope device array.  Each GPU the library runs on holds its own copy
+// until the process ends.  In host code the array's name is only a host-side
+// stand-in, never a device address: the address is looked up once per device
+// (with that device current) through hipGetSymbolAddress and kept in
+// g_scratch_dev, which is what kernels receive.
+constexpr size_t kStaticScratchBytes = BA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+ba_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch covers", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return BA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ba_status ba_prefix_attn_noalloc(const ba_attn_desc* desc, float* a_out, float* l_out, hipStream_t stream) {
+  g_err.clear();
+  AttnShape sh;
+  const ba_status st = check_desc(desc, &sh);
+  if (st != BA_OK) return st;
+  // the same plan (and so the same kernels and results) as ba_prefix_attn
+  const size_t need = prefix_ws_bytes(desc, plan_prefix(desc, sh.group));
+  if (need > kStaticScratchBytes)
+    return fail(BA_ERR_WORKSPACE,
+                "this call needs %zu bytes of split scratch; the static scratch holds %zu (use ba_prefix_attn "
+                "with a workspace)", need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && desc->n_seq > 0 && desc->max_q > 0) {
+    const ba_status s2 = static_scratch(&ws);
+    if (s2 != BA_OK) return s2;
+  }
+  return prefix_impl(desc, a_out, l_out, nullptr, nullptr, nullptr, nullptr, ws, ws ? kStaticScratchBytes : 0,
+                     stream);
 }
 
 ba_status ba_prefix_attn_rows(const ba_attn_desc* desc, const int32_t* cu_rows, const int32_t* rows, float* a_out,

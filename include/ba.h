@@ -114,6 +114,25 @@ ba_status ba_prefix_attn(const ba_attn_desc* desc, float* a_out, float* l_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ba_prefix_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Identical to ba_prefix_attn (same split plan, kernels and results) except
+ * that the split-KV partials go to a static scratch array inside the library
+ * instead of a caller workspace; the call allocates nothing and calls no
+ * allocating routine.  Each GPU holds one such array of
+ * BA_NOALLOC_SCRATCH_BYTES (64 MiB) from the library's first use on it until
+ * the process ends; a call whose split partials would not fit
+ * (ba_prefix_attn_workspace(desc) larger than that) returns
+ * BA_ERR_WORKSPACE and enqueues nothing.  The array of the device current at
+ * the call is used.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (different streams, or graphs replayed
+ * concurrently) race; calls in one stream's order do not.  Nothing in the
+ * array needs to start at zero: a call writes every partial it reads.
+ */
+#define BA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ba_status ba_prefix_attn_noalloc(const ba_attn_desc* desc, float* a_out, float* l_out, hipStream_t stream);
+
+/*
  * Partial refresh of the cached out-of-block part (FlashBlock, section 2,
  * "Estrategias de Reutilizacion Adaptativa": the cache is reused while few
  * block tokens change; here the rows that did change are recomputed and the

@@ -162,6 +162,27 @@ def test_fused_f32_validates_before_the_gate(lib):
     assert st == 1 and "a_in" in msg, (st, msg)
 
 
+def test_noalloc_rejects_scratch_beyond_its_limit(lib):
+    # 16 query heads of 3000 block rows on one KV head over a 30000-key
+    # prefix: 48000 rows per KV head in few workgroups, so the split plan's
+    # partials exceed the static scratch and the no-allocation call refuses
+    # it on the host (nothing is enqueued); the workspace call would take it.
+    d = lib_mod.AttnDesc()
+    d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, 1, 16, 1, 128, 3000, 30000
+    d.q = d.k = d.v = FAKE
+    for i, s in enumerate((3000 * 16 * 128, 16 * 128, 128)):
+        d.q_stride[i] = s
+    for i, s in enumerate((30000 * 128, 128, 30000 * 128)):
+        d.k_stride[i] = s
+        d.v_stride[i] = s
+    assert lib.ba_prefix_attn_workspace(ctypes.byref(d)) > lib_mod.BA_NOALLOC_SCRATCH_BYTES
+    st, msg = status_of(lib, lib.ba_prefix_attn_noalloc, ctypes.byref(d), FAKE, FAKE, None)
+    assert st == 5 and "static scratch" in msg, (st, msg)
+    d.d = 96
+    st, msg = status_of(lib, lib.ba_prefix_attn_noalloc, ctypes.byref(d), FAKE, FAKE, None)
+    assert st == 4 and "head dim" in msg, (st, msg)
+
+
 def test_prefix_empty_is_ok_without_launch(lib):
     d = good_desc()
     d.n_seq = 0
