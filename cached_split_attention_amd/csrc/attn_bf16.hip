@@ -51,6 +51,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "ba_internal.h"
 #include "gate_body.h"
 
@@ -385,6 +387,32 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[MB], u32x4 (&pk)[MB][2]
       for (int q = 0; q < 4; ++q) pk[mb][h2][q] = pack_bf16(s[mb][8 * h2 + 2 * q], s[mb][8 * h2 + 2 * q + 1]);
 }
 
+// The merge equation for one (row, head) entry: the weights of its two
+// parts and the merged log-normaliser; a part with L = -inf weighs nothing,
+// and both -inf give weights 0 and L = -inf.  The combine pass and the fused
+// merge of the in-block kernels both go through these two functions, so
+// they round alike.
+struct MergeWeights {
+  float w1, w2, l;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float l1, float l2) {
+  const float mm = fmaxf(l1, l2);
+  MergeWeights r{0.0f, 0.0f, -INFINITY};
+  if (mm != -INFINITY) {
+    const float e1 = __builtin_amdgcn_exp2f((l1 - mm) * kLog2e);
+    const float e2 = __builtin_amdgcn_exp2f((l2 - mm) * kLog2e);
+    const float den = e1 + e2;
+    const float rden = 1.0f / den;
+    r.w1 = e1 * rden;
+    r.w2 = e2 * rden;
+    r.l = mm + __logf(den);
+  }
+  return r;
+}
+__device__ __forceinline__ float merge_elem(const MergeWeights& w, float x1, float x2) {
+  return fmaf(w.w1, x1, w.w2 * x2);
+}
+
 // Where one lane's query row lives and what it writes.
 struct RowOut {
   int64_t orow;    // output row (packed row for varlen, else the dense row)
@@ -460,16 +488,8 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
   if (p.a_cache) {
     float lc;
     if constexpr (PREFETCH) lc = cache_l; else lc = p.l_cache[oe];
-    const float mm = fmaxf(lc, L);
-    float wc = 0.0f, wi = 0.0f, lf = -INFINITY, rden = 0.0f;
-    if (mm != -INFINITY) {
-      wc = __builtin_amdgcn_exp2f((lc - mm) * kLog2e);
-      wi = __builtin_amdgcn_exp2f((L - mm) * kLog2e);
-      const float den = wc + wi;
-      rden = 1.0f / den;
-      lf = mm + __logf(den);
-    }
-    const float fc = wc * rden, fi = wi * rden * inv;
+    // cache first, in-block part second, from the normalised A_in as stored
+    const MergeWeights mw = merge_weights(lc, L);
     if (p.a_full) {
       const float* ac = p.a_cache + oe * D;
       float* af = p.a_full + oe * D;
@@ -482,11 +502,11 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
           if constexpr (PREFETCH) cv = cache_a[db * 4 + j]; else cv = *reinterpret_cast<const f32x4*>(ac + c0);
           f32x4 val;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = fc * cv[e] + fi * o[db][4 * j + e];
+          for (int e = 0; e < 4; ++e) val[e] = merge_elem(mw, cv[e], o[db][4 * j + e] * inv);
           *reinterpret_cast<f32x4*>(af + c0) = val;
         }
     }
-    if (p.l_full && hf == 0) p.l_full[oe] = lf;
+    if (p.l_full && hf == 0) p.l_full[oe] = mw.l;
   }
 }
 
@@ -505,6 +525,13 @@ struct Item {
 // i % kXcds).  A group past n_splits * n_seq * hkv is no work.
 __device__ __forceinline__ int item_group(const AttnParams& p, int wg) {
   return (wg / kXcds / p.row_tiles) * kXcds + wg % kXcds;
+}
+
+// Workgroups of a part's grid: groups dealt to the XCDs in turn, each with
+// its row tiles (item_group numbers them).
+__host__ __device__ __forceinline__ int item_grid_size(const AttnParams& p) {
+  const int n_groups = p.n_splits * p.n_seq * p.hkv;
+  return kXcds * ((n_groups + kXcds - 1) / kXcds) * p.row_tiles;
 }
 
 template <int ROWS>
@@ -803,19 +830,14 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
 }
 
-// Alternating-phase kernel: 8 waves, 256 query rows, 64-key tiles in an
-// NS-stage ring.  Group grp (waves 4*grp .. 4*grp+3, rows 128*grp .. +127)
-// alternates matrix phases (O += P(u-1) V(u-1), then S(u) = K(u) Q^T) and
-// vector phases (softmax of S(u) into P(u)), group 1 one phase behind group
-// 0, so at every workgroup phase one group is in its matrix phase and the
-// other in its vector phase; waves w and w+4 share a SIMD.  Every wave passes
-// the same 2n+2 barriers (n tiles).  Tile u is waited for at workgroup phase
-// 2u and last read (as V by group 1) in phase 2u+3, so its stage can take
-// tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
-// u+1 .. u+NS-3 may still be in flight.
-template <int D, int NS, bool DUAL, bool GATE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
+// One work item of the alternating-phase kernel: (key split, sequence, KV
+// head, row tile) number wg of part p's grid.  gated: the part is gated by
+// decisions (with p.ready: read through the gate's ready words; ready_r >= 0
+// is the gate result already read).  Every wave of the workgroup returns
+// from it together.
+template <int D, int NS, bool GATE>
+__device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool gated, const int ready_r,
+                                        unsigned char* smem) {
   constexpr int NW = 8, ROWS = 256, KT = 64;
   constexpr int LOOK = NS - 2;   // tiles issued ahead of the one waited for
   static_assert(LOOK >= 1 && LOOK <= 3, "ring depth");
@@ -823,35 +845,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   constexpr int TILE_B = Dma::TILE_B;
   constexpr int STAGE_B = 2 * TILE_B;
   constexpr int KS = D / 16, DB = D / 32, MB = KT / 32;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE_B];
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
-
-  int bid = (int)blockIdx.x;
-  if constexpr (GATE) {
-    if (bid < grid_g) {
-      gate::run<true>(gp, bid, smem);
-      return;
-    }
-    bid -= grid_g;
-  }
-  const bool second = DUAL && bid >= grid0;
-  const AttnParams& p = second ? p1 : p0;
-  const int wg = second ? bid - grid0 : bid;
-  bool gated = p.decision != nullptr && p.mode != kBlock;
-  // A gated prefix workgroup reads its sequence's gate result first, from
-  // the prefix part's parameters alone (few dependent kernel-argument
-  // loads), and leaves at once when the whole sequence is reused: most
-  // prefix workgroups of a reuse step do only this.
-  int ready_r = -1;
-  if constexpr (GATE) {
-    if (second && p1.decision != nullptr && p1.ready != nullptr && p1.mode != kBlock) {
-      const int g = item_group(p1, wg);
-      if (g >= p1.n_splits * p1.n_seq * p1.hkv) return;
-      ready_r = gate_ready(p1, g / p1.n_splits / p1.hkv);
-      if (ready_r == 0) return;
-    }
-  }
-
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int grp = w >> 2;
@@ -962,6 +956,102 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
 }
 
+// Alternating-phase kernel: 8 waves, 256 query rows, 64-key tiles in an
+// NS-stage ring.  Group grp (waves 4*grp .. 4*grp+3, rows 128*grp .. +127)
+// alternates matrix phases (O += P(u-1) V(u-1), then S(u) = K(u) Q^T) and
+// vector phases (softmax of S(u) into P(u)), group 1 one phase behind group
+// 0, so at every workgroup phase one group is in its matrix phase and the
+// other in its vector phase; waves w and w+4 share a SIMD.  Every wave passes
+// the same 2n+2 barriers (n tiles).  Tile u is waited for at workgroup phase
+// 2u and last read (as V by group 1) in phase 2u+3, so its stage can take
+// tile u+NS from phase 2u+4 on: at phase 2u tile u+NS-2 is issued, and tiles
+// u+1 .. u+NS-3 may still be in flight.
+template <int D, int NS, bool DUAL, bool GATE, bool PERSIST = false>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
+  constexpr int STAGE_B = 2 * TileDma<D, 8, 64>::TILE_B;   // a K and a V tile of 64 keys
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE_B];
+
+  int bid = (int)blockIdx.x;
+  if constexpr (GATE) {
+    if (bid < grid_g) {
+      gate::run<true>(gp, bid, smem);
+      return;
+    }
+    bid -= grid_g;
+  }
+  const bool second = DUAL && bid >= grid0;
+  const int wg = second ? bid - grid0 : bid;
+  if constexpr (PERSIST) {
+    static_assert(GATE && DUAL, "the persistent prefix part belongs to a gated fused launch");
+    if (second) {
+      // Persistent gated prefix part of a count-gated step: prefix workgroup
+      // wg of p1.persist takes work items wg, wg + persist, ... of the part's
+      // grid.  Lane k of wave 0 reads the gate result of the k-th of them
+      // (up to 64 at once), and the workgroup computes those whose sequence
+      // recomputes (all of their heads).  The items of one sequence are
+      // consecutive, so a step that recomputes a few sequences spreads them
+      // over many workgroups, and a step that reuses everything costs each
+      // workgroup one round of reads.
+      __shared__ unsigned long long s_need;
+      const int stride = p1.persist;
+      const int n_items = item_grid_size(p1);
+      for (int k0 = wg; k0 < n_items; k0 += 64 * stride) {
+        if (threadIdx.x < 64) {
+          const int v = k0 + (int)threadIdx.x * stride;
+          bool need = false;
+          if (v < n_items) {
+            const int g = item_group(p1, v);
+            if (g < p1.n_splits * p1.n_seq * p1.hkv) {
+              const int32_t* word =
+                  p1.ready + (int)(blockIdx.x % kReadyCopies) * p1.ready_stride + g / p1.n_splits / p1.hkv;
+              const int r = gate::wait_ready_lane(word, gate::kCountReady, p1.spin_limit);
+              if (r < 0) {
+                if (p1.gave_up) atomicAdd(p1.gave_up, 1);
+                need = true;   // (split partials: the combine pass applies the decision)
+              } else {
+                need = (r & (gate::kCountReady - 1)) >= p1.gate_tau;
+              }
+            }
+          }
+          const unsigned long long bits = __builtin_amdgcn_ballot_w64(need);
+          if (threadIdx.x == 0) s_need = bits;
+        }
+        __syncthreads();
+        unsigned long long m = s_need;
+        __syncthreads();   // (s_need is rewritten by the next chunk)
+        while (m) {
+          const int k = __builtin_ctzll(m);
+          m &= m - 1;
+          pp_item<D, NS, GATE>(p1, k0 + k * stride, false, 1, smem);
+          __syncthreads();   // the next item's DMA reuses the ring stages
+        }
+      }
+      return;
+    }
+  }
+  // A gated prefix workgroup reads its sequence's gate result first, from
+  // the prefix part's parameters alone (few dependent kernel-argument
+  // loads), and leaves at once when the whole sequence is reused: most
+  // prefix workgroups of a reuse step do only this.
+  int ready_r = -1;
+  if constexpr (GATE) {
+    if (second && p1.decision != nullptr && p1.ready != nullptr && p1.mode != kBlock) {
+      const int g = item_group(p1, wg);
+      if (g >= p1.n_splits * p1.n_seq * p1.hkv) return;
+      ready_r = gate_ready(p1, g / p1.n_splits / p1.hkv);
+      if (ready_r == 0) return;
+    }
+  }
+
+  // (two calls rather than one on a reference chosen between the two
+  // parameter blocks, which would make the compiler copy both to scratch)
+  if (second)
+    pp_item<D, NS, GATE>(p1, wg, p1.decision != nullptr && p1.mode != kBlock, ready_r, smem);
+  else
+    pp_item<D, NS, GATE>(p0, wg, p0.decision != nullptr && p0.mode != kBlock, ready_r, smem);
+}
+
 // N-way log-space merge of the split-KV partials (the merge equation applied
 // across key splits), optionally followed by the merge with a precomputed
 // in-block part.  D/4 threads per (row, head) entry, four dims each.
@@ -1062,19 +1152,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     l_o = p.l[oo];
   }
   if (p.a_full) {
-    const float mm = fmaxf(l_o, li);
-    f32x4 af = {0.0f, 0.0f, 0.0f, 0.0f};
-    float lf = -INFINITY;
-    if (mm != -INFINITY) {
-      const float wo = __builtin_amdgcn_exp2f((l_o - mm) * kLog2e);
-      const float wi = __builtin_amdgcn_exp2f((li - mm) * kLog2e);
-      const float den = wo + wi;
-      const float rden = 1.0f / den;
-      af = (wo * rden) * a_o + (wi * rden) * ai;
-      lf = mm + __logf(den);
-    }
+    // prefix part (cached or fresh) first, in-block part second
+    const MergeWeights mw = merge_weights(l_o, li);
+    f32x4 af;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) af[e] = merge_elem(mw, a_o[e], ai[e]);
     *reinterpret_cast<f32x4*>(p.a_full + oo * D + 4 * t) = af;
-    if (t == 0 && p.l_full) p.l_full[oo] = lf;
+    if (t == 0 && p.l_full) p.l_full[oo] = mw.l;
   }
 }
 
@@ -1095,9 +1179,19 @@ namespace {
 
 // Groups (split, sequence, KV head) are dealt to the XCDs in turn, each with
 // its row tiles on consecutive workgroups of its XCD (decode_item).
-int item_grid(const AttnParams& p) {
-  const int n_groups = p.n_splits * p.n_seq * p.hkv;
-  return kXcds * ((n_groups + kXcds - 1) / kXcds) * p.row_tiles;
+int item_grid(const AttnParams& p) { return item_grid_size(p); }
+
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 // p1 == nullptr: one part.  With two parts, p1's workgroups come first in
@@ -1142,8 +1236,22 @@ hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, const GateParam
   const int g1 = item_grid(*p1);
   if (g) {
     const int gg = gate_grid(*g);
-    hipLaunchKernelGGL((attn_pp_kernel<D, NS, true, true>), dim3(gg + g0 + g1), dim3(512), 0, s, *p1, p0, g1, *g,
-                       gg);
+    // A gated step under a count gate decides per sequence: its prefix part
+    // runs as one persistent workgroup per compute unit (one fits per CU)
+    // over the work items, reading their gate results in one batch.
+    AttnParams pp = p0;
+    int gp = g0;
+    if (p0.decision != nullptr && p0.ready != nullptr && g->mode != BA_GATE_COSINE) {
+      // (at most 64 items each: one pre-pass read per lane of a wave)
+      pp.persist = std::min(g0, std::max(device_cus(), (g0 + 63) / 64));
+      gp = pp.persist;
+    }
+    if (pp.persist > 0)
+      hipLaunchKernelGGL((attn_pp_kernel<D, NS, true, true, true>), dim3(gg + gp + g1), dim3(512), 0, s, *p1, pp, g1,
+                         *g, gg);
+    else
+      hipLaunchKernelGGL((attn_pp_kernel<D, NS, true, true>), dim3(gg + gp + g1), dim3(512), 0, s, *p1, pp, g1, *g,
+                         gg);
     return hipGetLastError();
   }
   if (g0 + g1 == 0) return hipSuccess;

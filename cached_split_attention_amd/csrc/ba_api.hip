@@ -102,7 +102,13 @@ struct PrefixPlan {
 // weighted 1, whose workgroups only read their decision and leave (about
 // half a tile each, per round of slots).  shares == 0: ungated, the full
 // share only.
-PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 0) {
+// per_seq: the gate decides per sequence (count gates).  With the 256-row
+// kernel such a gated step runs its prefix part as persistent workgroups
+// (one per compute unit) that read their items' gate results in one batch:
+// a step that reuses everything then costs about one round of reads
+// whatever the split, and the combine pass only handles the recomputing
+// share's partials, so both terms are modelled that way.
+PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int shares = 0, bool per_seq = false) {
   PrefixPlan pp{};
   if (d->dtype == BA_F32) {
     pp.row_tiles = 1;
@@ -132,20 +138,26 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   double best_cost = 1e300;
   const bool gated = shares >= 1;
   if (!gated) shares = 1;
+  const bool persistent = gated && per_seq && pp.bf.variant == 3;
+  auto comb_of = [&](int64_t se, int64_t it) {
+    return se > 1 ? 2.0 + (double)se * it * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
+  };
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
     double span = 0.0, wsum = 0.0;
     for (int k = shares; k >= 1; --k) {
       const int64_t it = (items * k + shares - 1) / shares;
-      span += (double)((it * se + slots - 1) / slots) * (double)(ci + 2) / k;
+      double term = (double)((it * se + slots - 1) / slots) * (double)(ci + 2);
+      if (persistent) term += comb_of(se, it);
+      span += term / k;
       wsum += 1.0 / k;
     }
     if (gated) {
-      span += 0.5 * (double)((items * se + slots - 1) / slots);
+      span += 0.5 * (persistent ? 1.0 : (double)((items * se + slots - 1) / slots));
       wsum += 1.0;
     }
-    const double comb = se > 1 ? 2.0 + (double)se * items * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
+    const double comb = persistent ? 0.0 : comb_of(se, items);
     const double cost = span / wsum + comb;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
@@ -235,6 +247,9 @@ int gate_shares(const ba::GateParams* gate, const ba_attn_desc* desc) {
   return gate->mode == BA_GATE_COSINE ? kMaxShares : seq_shares(desc->n_seq);
 }
 
+// Whether a gated fused step decides per sequence (count gates).
+bool gate_per_seq(const ba::GateParams* gate) { return gate && gate->mode != BA_GATE_COSINE; }
+
 }  // namespace
 
 // Covers every plan a descriptor can get (ungated, and the gated fused
@@ -243,8 +258,9 @@ size_t ba_prefix_attn_workspace(const ba_attn_desc* desc) {
   AttnShape sh;
   if (check_desc(desc, &sh) != BA_OK) return 0;
   size_t need = 0;
-  for (int shares : {0, seq_shares(desc->n_seq), kMaxShares}) {
-    const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, shares), shares > 0);
+  const int plans[3][2] = {{0, 0}, {seq_shares(desc->n_seq), 1}, {kMaxShares, 0}};   // (shares, per sequence)
+  for (const auto& pl : plans) {
+    const size_t b = prefix_ws_bytes(desc, plan_prefix(desc, sh.group, -1, pl[0], pl[1] != 0), pl[0] > 0);
     if (b > need) need = b;
   }
   return need;
@@ -270,7 +286,8 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_NULL, "the merge needs a_in, l_in and a_full");
   if (merge && (!aligned16(a_in) || !aligned16(a_full) || !aligned16(a_out)))
     return fail(BA_ERR_UNSUPPORTED, "a_out, a_in and a_full must be 16-byte aligned");
-  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 0 : gate_shares(gate, desc));
+  const PrefixPlan pp = plan_prefix(desc, sh.group, kblocks ? n_kblocks : -1, kblocks ? 0 : gate_shares(gate, desc),
+                                    !kblocks && gate_per_seq(gate));
   // a gated fused step's prefix workgroups may give up waiting for the gate:
   // their results then go through the split workspace (see prefix_ws_bytes)
   const bool always_partial = partial_always(desc, gate != nullptr && desc->decision != nullptr);

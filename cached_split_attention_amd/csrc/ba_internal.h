@@ -54,6 +54,11 @@ struct AttnParams {
   int ready_stride;
   int spin_limit;
   int32_t* gave_up;
+  // > 0: the gated prefix part of a count-gated fused launch runs as this
+  // many persistent workgroups, workgroup i taking work items i, i + persist,
+  // ... of the part's grid and computing only those whose sequence
+  // recomputes.
+  int persist;
   int gate_mode;
   int gate_tau;
   // Key-block list mode (dense prefix only): (sequence, KV head) attends over

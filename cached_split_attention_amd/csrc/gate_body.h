@@ -406,5 +406,21 @@ __device__ __forceinline__ int wait_ready(const int32_t* word, int target, int l
   return -1;
 }
 
+// As wait_ready, but each lane waits for its own word (the lanes of a wave
+// may poll different words): returns this lane's word, or -1 after `limit`
+// polls.
+__device__ __forceinline__ int wait_ready_lane(const int32_t* word, int target, int limit) {
+  int r = -1;
+  for (int n = 0; n < limit; ++n) {
+    const int x = ld_agent(word);
+    if (x >= target) {
+      r = x;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return r;
+}
+
 }  // namespace gate
 }  // namespace ba

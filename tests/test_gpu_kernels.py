@@ -780,17 +780,19 @@ def test_gated_split_attn_finer_split(mode):
     assert not host(gws).view(np.int32).any(), "gate workspace not left zero"
 
 
-@pytest.mark.parametrize("lp", [512, 64])
+@pytest.mark.parametrize("lp,hkv,nb", [(512, 8, 32), (64, 8, 32), (1000, 2, 64)])
 @pytest.mark.parametrize("mode", ["count", "cosine"])
-def test_gated_split_attn_gives_up(mode, lp):
+def test_gated_split_attn_gives_up(mode, lp, hkv, nb):
     # The prefix workgroups' bounded wait for the gate, forced to give up at
-    # once from the host (wait_polls < 0): every gated prefix workgroup is
-    # counted and computes its heads into the split workspace, and the
-    # combine pass, which runs after the gate, applies the gate's decisions.
-    # So the outputs equal those of the gate followed by the split pass, with
+    # once from the host (wait_polls < 0): every gated prefix work item is
+    # counted and computed into the split workspace, and the combine pass,
+    # which runs after the gate, applies the gate's decisions.  So the
+    # outputs equal those of the gate followed by the split pass, with
     # several key splits (lp 512) and with one (lp 64), and reused heads keep
-    # their cache bit for bit.
-    B, hq, hkv, d, nb = 2, 8, 8, 128, 32
+    # their cache bit for bit.  256 rows per KV head (hkv 2, nb 64) run the
+    # 256-row kernel, whose count-gated steps use persistent prefix
+    # workgroups.
+    B, hq, d = 2, 8, 128
     s = _dense_inputs("bf16", B, hq, hkv, d, lp, nb, seed=93)
     rows = B * nb
     q, k, v = dev_in(s.q[0], "bf16"), dev_in(s.k[0], "bf16"), dev_in(s.v[0], "bf16")
