@@ -3,6 +3,8 @@
 // nothing was enqueued.
 
 #include <math.h>
+
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -142,13 +144,22 @@ PrefixPlan plan_prefix(const ba_attn_desc* d, int group, int n_kblocks = -1, int
   auto comb_of = [&](int64_t se, int64_t it) {
     return se > 1 ? 2.0 + (double)se * it * pp.bf.rows_per_wg / ((double)kpi * slots) : 0.0;
   };
+  // Workgroups with keys to stream.  In varlen mode the key counts are
+  // device data, so a sequence is taken to hold about 0.65 of max_k keys
+  // (the splits past its end exit at once); for the multi-branch batch's
+  // prefixes (2048 .. 8192 keys) this picks the split whose busy workgroups
+  // fit one round of slots.
+  const bool varlen = d->cu_q != nullptr;
+  auto busy = [&](int64_t it, int64_t se) {
+    return varlen ? it * (int64_t)std::ceil(0.65 * (double)se) : it * se;
+  };
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t ci = (iters + s - 1) / s;
     const int64_t se = ci > 0 ? (iters + ci - 1) / ci : 1;
     double span = 0.0, wsum = 0.0;
     for (int k = shares; k >= 1; --k) {
       const int64_t it = (items * k + shares - 1) / shares;
-      double term = (double)((it * se + slots - 1) / slots) * (double)(ci + 2);
+      double term = (double)((busy(it, se) + slots - 1) / slots) * (double)(ci + 2);
       if (persistent) term += comb_of(se, it);
       span += term / k;
       wsum += 1.0 / k;
