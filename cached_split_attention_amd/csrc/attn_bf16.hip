@@ -510,6 +510,58 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
   }
 }
 
+// Epilogue of the 256-row kernel for the modes without the fused merge
+// (split partial, final prefix result, A_in/L_in): the wave's normalised
+// 32 x D block goes through its own LDS region (the ring is free once every
+// tile is consumed), so that each global store writes whole rows (D floats
+// contiguous) instead of a 32-byte piece of each of 32 rows.  In LDS, row rr
+// keeps its 16-byte chunk c at position c ^ (rr mod chunks per row), so the
+// row-owning writes and the chunk-owning reads both spread over the banks.
+// Every wave of the workgroup must call it (it starts with a barrier).
+template <int D>
+__device__ __forceinline__ void write_result_staged(const AttnParams& p, int mode, bool writer, const RowOut& ro,
+                                                    const f32x16 (&o)[D / 32], float m_run, float l_tot,
+                                                    unsigned char* wave_lds) {
+  constexpr int DB = D / 32;
+  constexpr int CH = D / 4;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;       // rows per wave-wide store
+  const int lane = (int)threadIdx.x & 63;
+  const int lr = lane & 31, hf = ro.hf;
+  const bool has = l_tot > 0.0f;
+  const float inv = has ? 1.0f / l_tot : 0.0f;
+  const float L = has ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // destination entry of this lane's row (-1: not written)
+  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  const bool partial = mode == kPrefixPartial;
+  float* a_base = partial ? p.ws_a : p.a;
+  float* l_base = partial ? p.ws_l : p.l;
+  const int64_t ent = partial ? (int64_t)ro.split * n_entries + ro.prow * p.hq + ro.h : ro.orow * p.hq + ro.h;
+  const int my_ent = writer ? (int)ent : -1;
+
+  wait_vmem_all();
+  __syncthreads();   // every wave is done with the ring
+  f32x4* rowp = reinterpret_cast<f32x4*>(wave_lds + lr * (D * 4));
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = db * 8 + 2 * j + hf;
+      rowp[c ^ (lr & (CH - 1))] = f32x4{o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
+                                        o[db][4 * j + 3] * inv};
+    }
+  if (a_base) {
+    const int cc = lane % CH;
+#pragma unroll
+    for (int s = 0; s < 32 / RPI; ++s) {
+      const int rr = RPI * s + lane / CH;
+      const int e = __shfl(my_ent, rr);
+      const f32x4 val = reinterpret_cast<const f32x4*>(wave_lds + rr * (D * 4))[cc ^ (rr & (CH - 1))];
+      if (e >= 0) *reinterpret_cast<f32x4*>(a_base + (int64_t)e * D + 4 * cc) = val;
+    }
+  }
+  if (l_base && writer && hf == 0) l_base[ent] = L;
+}
+
 // Work item of a workgroup covering ROWS query rows: (sequence, KV head,
 // row tile, key split) and the sequence's query/key ranges.
 struct Item {
@@ -631,14 +683,10 @@ __device__ __forceinline__ int gate_ready(const AttnParams& p, int b) {
   return s_r;
 }
 
-// A launch may carry two independent parts (the prefix and the in-block
-// attention of one step): workgroups [0, grid0) run part p0, the rest p1.
-// With GATE, the reuse gate gp runs first, in workgroups [0, grid_g), and
-// the rest are numbered from there.
-template <int D, int RW, int KW, int KT, int ST, bool DUAL, bool GATE>
-__global__ void __launch_bounds__(64 * RW * KW)
-    __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
-attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
+// One work item of the row-wave/key-wave kernel: number wg of part p's
+// grid.  Every wave of the workgroup returns from it together.
+template <int D, int RW, int KW, int KT, int ST, bool GATE>
+__device__ __forceinline__ void bf16_item(const AttnParams& p, const int wg, unsigned char* smem) {
   constexpr int NW = RW * KW;
   constexpr int KTILE = KW * KT;                 // keys per iteration tile
   using Dma = TileDma<D, NW, KTILE>;
@@ -652,20 +700,8 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
   constexpr int SMEM_R = ST * STAGE_B;
   constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
-  int bid = (int)blockIdx.x;
-  if constexpr (GATE) {
-    if (bid < grid_g) {
-      gate::run<false>(gp, bid, smem);
-      return;
-    }
-    bid -= grid_g;
-  }
-  const bool second = DUAL && bid >= grid0;
-  const AttnParams& p = second ? p1 : p0;
-  const int wg = second ? bid - grid0 : bid;
   bool gated = p.decision != nullptr && p.mode != kBlock;
 
   const int tid = threadIdx.x;
@@ -827,7 +863,40 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
   if (gated) writer = writer && !reused(p, b, h);
   const RowOut ro{qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
+  // (the LDS-staged epilogue of the 256-row kernel measured slower here: the
+  // LLaDA-like prefix pass took 21.2 us against 19.8)
   write_result<D, kPrefetchCache>(p, itm.mode, writer, ro, o, m_run, l_tot, cache_a, cache_l);
+}
+
+// A launch may carry two independent parts (the prefix and the in-block
+// attention of one step): workgroups [0, grid0) run part p0, the rest p1.
+// With GATE, the reuse gate gp runs first, in workgroups [0, grid_g), and
+// the rest are numbered from there.
+template <int D, int RW, int KW, int KT, int ST, bool DUAL, bool GATE>
+__global__ void __launch_bounds__(64 * RW * KW)
+    __attribute__((amdgpu_waves_per_eu(ST * 4 * KW * KT * D > 80 * 1024 ? 1 : 2)))
+attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GateParams gp, int grid_g) {
+  constexpr int KTILE = KW * KT;
+  constexpr int TILE_B = TileDma<D, RW * KW, KTILE>::TILE_B;
+  constexpr int XSLOT = (D / 32 * 16 + 2) * 64;
+  constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
+  constexpr int SMEM_R = ST * 2 * TILE_B;
+  constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  int bid = (int)blockIdx.x;
+  if constexpr (GATE) {
+    if (bid < grid_g) {
+      gate::run<false>(gp, bid, smem);
+      return;
+    }
+    bid -= grid_g;
+  }
+  // (two calls rather than one on a reference chosen between the two
+  // parameter blocks, which would make the compiler copy both to scratch)
+  if (DUAL && bid >= grid0)
+    bf16_item<D, RW, KW, KT, ST, GATE>(p1, bid - grid0, smem);
+  else
+    bf16_item<D, RW, KW, KT, ST, GATE>(p0, bid, smem);
 }
 
 // One work item of the alternating-phase kernel: (key split, sequence, KV
@@ -953,7 +1022,10 @@ __device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool 
   if (gated) writer = writer && !reused(p, b, h);
   const RowOut ro{qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
-  write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
+  if (itm.mode == kBlock && p.a_cache)
+    write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
+  else
+    write_result_staged<D>(p, itm.mode, writer, ro, o, m_run, l_tot, smem + w * (32 * D * 4));
 }
 
 // Alternating-phase kernel: 8 waves, 256 query rows, 64-key tiles in an
