@@ -42,10 +42,12 @@
 //                     group's wave on a SIMD issues MFMAs the other's issues
 //                     the exponentials, so the matrix cores are not left idle
 //                     during the softmax.  Serves long row counts.
-// Work mapping: workgroup i runs on XCD i % 8.  Work items are groups
-// (key split, sequence, KV head), split fastest, each with its row tiles;
-// group g goes to XCD g % 8 and its row tiles (which read the same K/V
-// tiles) to consecutive workgroups there, so their re-reads hit that XCD's
+// Work mapping: workgroups i and j of a launch run on the same XCD exactly
+// when i = j (mod 8) (which XCD takes class 0 rotates between launches).
+// Work items are groups (key split, sequence, KV head), split fastest,
+// each with its row tiles; group g goes to XCD class g % 8 and its row
+// tiles (which read the same K/V tiles) to consecutive workgroups of that
+// class, so their re-reads hit that XCD's
 // L2, while the groups of any subset of sequences or heads -- what a gated
 // step recomputes -- spread over all XCDs.
 
@@ -573,8 +575,9 @@ struct Item {
 
 // Work item group (key split, sequence, KV head; split fastest) of
 // workgroup wg: groups are dealt to the XCDs in turn, each with its row
-// tiles on consecutive workgroups of its XCD (workgroup i runs on XCD
-// i % kXcds).  A group past n_splits * n_seq * hkv is no work.
+// tiles on consecutive workgroups of its XCD (workgroups whose numbers are
+// congruent mod kXcds share an XCD).  A group past n_splits * n_seq * hkv
+// is no work.
 __device__ __forceinline__ int item_group(const AttnParams& p, int wg) {
   return (wg / kXcds / p.row_tiles) * kXcds + wg % kXcds;
 }

@@ -1293,22 +1293,29 @@ def test_schedule_bf16(schedule, gate):
     assert _run_schedule(s) > 0
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("gate,hkv,nb", [
+    ("count", 2, 33),     # 128-row tiles: gate, attention launch, then the combine pass
+    ("count", 1, 80),     # 256-row kernel, one launch per step (persistent prefix part)
+    ("cosine", 1, 80),    # 256-row kernel, one launch per step
+])
+def test_graph_replay_matches_eager(gate, hkv, nb):
     """A captured block schedule replays to the eager result, every time,
-    with eager work and synchronisations between the replays."""
-    s = make_block_schedule(dtype="bf16", B=2, hq=4, hkv=2, d=128, lp=900, nb=33, steps=4, std=1.0,
-                            schedule="redraw", redraw_range=(0, 3), gate="count", tau=2, seed=68)
+    with eager work and synchronisations between the replays (the launches'
+    synchronisation words must be left cleared for the next replay)."""
+    s = make_block_schedule(dtype="bf16", B=2, hq=4, hkv=hkv, d=128, lp=900, nb=nb, steps=4, std=1.0,
+                            schedule="redraw", redraw_range=(0, 3), sigma_range=(0.01, 0.5), gate=gate, tau=2,
+                            gamma=0.95, seed=68)
     kp, vp = dev_bits(s.kp), dev_bits(s.vp)
     q = [dev_bits(x) for x in s.q]
     k = [dev_bits(x) for x in s.k]
     v = [dev_bits(x) for x in s.v]
-    eager = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate="count", tau=s.tau)
+    eager = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate=gate, tau=s.tau, gamma=s.gamma)
     outs = []
     for t in range(1, s.steps + 1):
         af, lf = eager.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
         outs.append((af.clone(), lf.clone(), eager.a_out.clone(), eager.decision.clone()))
     torch.cuda.synchronize()
-    attn = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate="count", tau=s.tau)
+    attn = ba.CachedBlockAttention(kp, vp, nb=s.nb, hq=s.hq, gate=gate, tau=s.tau, gamma=s.gamma)
     g = attn.capture_block(q, k, v)
     g1 = attn.capture(q, k, v, [s.steps], new_block=False)
     for rep in range(3):
