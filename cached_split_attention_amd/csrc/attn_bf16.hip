@@ -519,6 +519,8 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
 // contiguous) instead of a 32-byte piece of each of 32 rows.  In LDS, row rr
 // keeps its 16-byte chunk c at position c ^ (rr mod chunks per row), so the
 // row-owning writes and the chunk-owning reads both spread over the banks.
+// The stores are nontemporal: the rows are read back by the next pass, not
+// by this one (the GQA reuse step measured 20.9 -> 19.8 us with them).
 // Every wave of the workgroup must call it (it starts with a barrier).
 template <int D>
 __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mode, bool writer, const RowOut& ro,
@@ -558,7 +560,7 @@ __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mod
       const int rr = RPI * s + lane / CH;
       const int e = __shfl(my_ent, rr);
       const f32x4 val = reinterpret_cast<const f32x4*>(wave_lds + rr * (D * 4))[cc ^ (rr & (CH - 1))];
-      if (e >= 0) *reinterpret_cast<f32x4*>(a_base + (int64_t)e * D + 4 * cc) = val;
+      if (e >= 0) __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(a_base + (int64_t)e * D + 4 * cc));
     }
   }
   if (l_base && writer && hf == 0) l_base[ent] = L;
@@ -1127,28 +1129,41 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
     pp_item<D, NS, GATE>(p0, wg, p0.decision != nullptr && p0.mode != kBlock, ready_r, smem);
 }
 
-// N-way log-space merge of the split-KV partials (the merge equation applied
-// across key splits), optionally followed by the merge with a precomputed
-// in-block part.  D/4 threads per (row, head) entry, four dims each.
-//   p.mode == kPrefixPartial: entries whose prefix was recomputed combine the
-//     split partials into A_out/L_out (p.a, p.l); the L and A partials of up
-//     to 16 splits are loaded together, so one memory round trip serves a
-//     batch.  Entries of reused heads (or of sequences with no prefix keys)
-//     keep the A_out/L_out already in p.a/p.l.
-//   p.mode == kPrefixFinal: A_out/L_out are already in p.a/p.l.
-//   p.a_full != NULL: A_full/L_full = merge(A_out, L_out, A_in, L_in) with
-//     A_in/L_in in p.a_cache/p.l_cache, for every entry.
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// One entry of the combine: where it lives and what its first memory round
+// trip brought (the in-block part and, speculatively, the cached prefix
+// result, loaded together with the decision).
+struct CombineEntry {
+  int64_t oo;     // output entry (row * hq + head); -1: nothing to do
+  int64_t e;      // dense entry (split partials are laid out by it)
+  int units;      // keys, or listed key blocks
+  bool fresh;     // the prefix was recomputed: combine the split partials
+  float li, l_c;
+  f32x4 ai, a_c;
+};
+
 template <int D>
-__global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
-  constexpr int TPE = D / 4;
-  constexpr int EPB = 256 / TPE;
-  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
-  if (p.ready && blockIdx.x == 0)
-    for (int c = 0; c < kReadyCopies; ++c)
-      for (int b = threadIdx.x; b < p.n_seq; b += blockDim.x) p.ready[c * p.ready_stride + b] = 0;
-  const int64_t e = (int64_t)blockIdx.x * EPB + threadIdx.x / TPE;
-  const int t = threadIdx.x % TPE;
-  if (e >= n_entries) return;
+__device__ __forceinline__ CombineEntry combine_load(const AttnParams& p, int64_t e, int t, int64_t n_entries) {
+  CombineEntry x;
+  x.oo = -1;
+  x.e = e;
+  x.units = 0;
+  x.fresh = false;
+  x.li = x.l_c = 0.0f;
+  x.ai = x.a_c = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (e >= n_entries) return x;
   const int h = (int)(e % p.hq);
   const int64_t vrow = e / p.hq;
   const int b = (int)(vrow / p.max_q);
@@ -1159,35 +1174,38 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     nq = min(max(p.cu_q[b + 1] - qbase, 0), p.max_q);
   }
   if (p.cu_k) nk = p.cu_k[b + 1] - p.cu_k[b];
-  if (i >= nq) return;
+  if (i >= nq) return x;
   const int64_t orow = p.q_rows ? (int64_t)b * p.max_q + listed_row(p, b, qbase + i)
                                 : (p.cu_q ? (int64_t)(qbase + i) : vrow);
   const int64_t oo = orow * p.hq + h;
-  // With a decision to read, the loads that do not depend on it (the in-block
-  // part and, speculatively, the cached A_out/L_out) go out with it, so a
-  // reused entry costs one memory round trip.
-  float li = 0.0f, l_c = 0.0f;
-  f32x4 ai = {0.0f, 0.0f, 0.0f, 0.0f}, a_c = ai;
-  const bool spec = p.decision && p.a_full;
+  // (these loads go out before the decision is looked at: one round trip)
+  // (nontemporal: each is read once)
   if (p.a_full) {
-    li = p.l_cache[oo];
-    ai = *reinterpret_cast<const f32x4*>(p.a_cache + oo * D + 4 * t);
+    x.li = p.l_cache[oo];
+    x.ai = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.a_cache + oo * D + 4 * t));
+    if (p.decision) {
+      x.l_c = p.l[oo];
+      x.a_c = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t));
+    }
   }
-  if (spec) {
-    l_c = p.l[oo];
-    a_c = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
-  }
+  x.units = p.kblocks ? p.n_kblocks : nk;
   // An empty prefix is written by the attention kernel's split 0.
-  const bool fresh = p.mode == kPrefixPartial && (p.kblocks ? p.n_kblocks : nk) > 0 &&
-                     !(p.decision && p.decision[b * p.hq + h]);
-  if (!fresh && !p.a_full) return;
+  x.fresh = p.mode == kPrefixPartial && x.units > 0 && !(p.decision && p.decision[b * p.hq + h]);
+  if (x.fresh || p.a_full) x.oo = oo;   // (else nothing to write)
+  return x;
+}
+
+template <int D>
+__device__ __forceinline__ void combine_finish(const AttnParams& p, const CombineEntry& x, int t,
+                                               int64_t n_entries) {
+  if (x.oo < 0) return;
+  const int64_t oo = x.oo;
   f32x4 a_o;
   float l_o;
-  if (fresh) {
-    const int units = p.kblocks ? p.n_kblocks : nk;   // keys, or listed key blocks
-    const int ns = (units + p.chunk - 1) / p.chunk;
-    const float* la = p.ws_l + e;
-    const float* aa = p.ws_a + e * D + 4 * t;
+  if (x.fresh) {
+    const int ns = (x.units + p.chunk - 1) / p.chunk;
+    const float* la = p.ws_l + x.e;
+    const float* aa = p.ws_a + x.e * D + 4 * t;
     const int64_t cs = n_entries;
     float mx = -INFINITY, den = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1199,7 +1217,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
       for (int u = 0; u < CB; ++u) {
         const bool ok = c0 + u < ns;
         lv[u] = ok ? la[(c0 + u) * cs] : -INFINITY;
-        av[u] = ok ? *reinterpret_cast<const f32x4*>(aa + (c0 + u) * cs * D) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        av[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(aa + (c0 + u) * cs * D))
+                   : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
       float bm = mx;
 #pragma unroll
@@ -1217,23 +1236,58 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
     }
     a_o = acc * (1.0f / den);
     l_o = mx + __logf(den);
-    *reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t) = a_o;
+    __builtin_nontemporal_store(a_o, reinterpret_cast<f32x4*>(p.a + oo * D + 4 * t));
     if (t == 0) p.l[oo] = l_o;
-  } else if (spec) {
-    a_o = a_c;
-    l_o = l_c;
+  } else if (p.decision) {
+    a_o = x.a_c;
+    l_o = x.l_c;
   } else {
     a_o = *reinterpret_cast<const f32x4*>(p.a + oo * D + 4 * t);
     l_o = p.l[oo];
   }
   if (p.a_full) {
     // prefix part (cached or fresh) first, in-block part second
-    const MergeWeights mw = merge_weights(l_o, li);
+    const MergeWeights mw = merge_weights(l_o, x.li);
     f32x4 af;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) af[e] = merge_elem(mw, a_o[e], ai[e]);
-    *reinterpret_cast<f32x4*>(p.a_full + oo * D + 4 * t) = af;
+    for (int k = 0; k < 4; ++k) af[k] = merge_elem(mw, a_o[k], x.ai[k]);
+    __builtin_nontemporal_store(af, reinterpret_cast<f32x4*>(p.a_full + oo * D + 4 * t));
     if (t == 0 && p.l_full) p.l_full[oo] = mw.l;
+  }
+}
+
+// N-way log-space merge of the split-KV partials (the merge equation applied
+// across key splits), optionally followed by the merge with a precomputed
+// in-block part.  D/4 threads per (row, head) entry, four dims each; a
+// workgroup takes PER groups of 256/(D/4) consecutive entries (groups g and
+// g + gridDim.x when PER == 2), whose first loads go out together.
+//   p.mode == kPrefixPartial: entries whose prefix was recomputed combine the
+//     split partials into A_out/L_out (p.a, p.l); the L and A partials of up
+//     to 16 splits are loaded together, so one memory round trip serves a
+//     batch.  Entries of reused heads (or of sequences with no prefix keys)
+//     keep the A_out/L_out already in p.a/p.l.
+//   p.mode == kPrefixFinal: A_out/L_out are already in p.a/p.l.
+//   p.a_full != NULL: A_full/L_full = merge(A_out, L_out, A_in, L_in) with
+//     A_in/L_in in p.a_cache/p.l_cache, for every entry.
+template <int D, int PER>
+__global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
+  constexpr int TPE = D / 4;
+  constexpr int EPB = 256 / TPE;
+  const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
+  if (p.ready && blockIdx.x == 0)
+    for (int c = 0; c < kReadyCopies; ++c)
+      for (int b = threadIdx.x; b < p.n_seq; b += blockDim.x) p.ready[c * p.ready_stride + b] = 0;
+  const int t = threadIdx.x % TPE;
+  const int64_t e0 = (int64_t)blockIdx.x * EPB + threadIdx.x / TPE;
+  if constexpr (PER == 1) {
+    const CombineEntry x = combine_load<D>(p, e0, t, n_entries);
+    combine_finish<D>(p, x, t, n_entries);
+  } else {
+    const int64_t e1 = e0 + (int64_t)gridDim.x * EPB;
+    const CombineEntry x0 = combine_load<D>(p, e0, t, n_entries);
+    const CombineEntry x1 = combine_load<D>(p, e1, t, n_entries);
+    combine_finish<D>(p, x0, t, n_entries);
+    combine_finish<D>(p, x1, t, n_entries);
   }
 }
 
@@ -1242,11 +1296,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p) {
 hipError_t launch_combine(const AttnParams& p, int d, hipStream_t s) {
   const int64_t n_entries = (int64_t)p.n_seq * p.max_q * p.hq;
   const int64_t epb = 256 / (d / 4);
-  const dim3 grid((unsigned)((n_entries + epb - 1) / epb));
-  if (d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, s, p);
+  const int64_t groups = (n_entries + epb - 1) / epb;
+  // Large passes: two entry groups per workgroup (half the workgroups to
+  // dispatch, two entries' loads in flight per thread); small ones keep one
+  // group each, for more workgroups.
+  const bool two = groups > 4 * (int64_t)device_cus();
+  const dim3 grid((unsigned)(two ? (groups + 1) / 2 : groups));
+  if (d == 128) {
+    if (two) hipLaunchKernelGGL((combine_kernel<128, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(256), 0, s, p);
+  } else {
+    if (two) hipLaunchKernelGGL((combine_kernel<64, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<64, 1>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -1256,18 +1318,6 @@ namespace {
 // its row tiles on consecutive workgroups of its XCD (decode_item).
 int item_grid(const AttnParams& p) { return item_grid_size(p); }
 
-// Compute units of the current device (looked up once per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // p1 == nullptr: one part.  With two parts, p1's workgroups come first in
 // the grid (dispatch order): the caller passes the in-block part as p1, so
