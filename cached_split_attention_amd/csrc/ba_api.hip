@@ -80,6 +80,10 @@ ba_status check_desc(const ba_attn_desc* d, AttnShape* out) {
   if ((int64_t)d->n_seq * d->hkv > 65535 && !varlen)
     return fail(BA_ERR_UNSUPPORTED, "n_seq * hkv = %lld exceeds 65535", (long long)d->n_seq * d->hkv);
   if ((int64_t)d->n_seq * d->hkv > 65535) return fail(BA_ERR_UNSUPPORTED, "n_seq * hkv exceeds 65535");
+  // (rows per KV head, hq / hkv * max_q, are numbered with 32-bit integers)
+  if ((int64_t)(d->hq / d->hkv) * d->max_q > (1LL << 30))
+    return fail(BA_ERR_UNSUPPORTED, "hq / hkv * max_q = %lld rows per KV head exceeds 2^30",
+                (long long)(d->hq / d->hkv) * d->max_q);
   out->group = d->hq / d->hkv;
   out->varlen = varlen;
   out->scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)d->d);
@@ -307,6 +311,11 @@ ba_status prefix_impl(const ba_attn_desc* desc, float* a_out, float* l_out, cons
     return fail(BA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if ((int64_t)pp.n_splits * pp.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
     return fail(BA_ERR_UNSUPPORTED, "too many workgroups");
+  // (the 256-row kernel's staged epilogue indexes (split, row, head)
+  // entries with 32-bit integers)
+  if (desc->dtype == BA_BF16 && pp.bf.variant == 3 &&
+      (int64_t)pp.n_splits * desc->n_seq * desc->max_q * desc->hq > 0x7fffffffLL)
+    return fail(BA_ERR_UNSUPPORTED, "too many (split, row, head) entries");
   ba::AttnParams p = base_params(desc, sh);
   p.decision = desc->decision;
   p.chunk = pp.chunk;

@@ -78,6 +78,9 @@ typedef enum { BA_GATE_COUNT = 0, BA_GATE_COSINE = 1, BA_GATE_COUNT_CUM = 2, BA_
  * decision: optional device uint8[n_seq, hq] as written by ba_reuse_gate;
  *   1 = keep the cached A_out/L_out of that (sequence, head), 0 = recompute.
  *   NULL = recompute everything.  Only ba_prefix_attn reads it.
+ * Limits (BA_ERR_UNSUPPORTED beyond them): n_seq * hkv <= 65535 in dense
+ *   mode; hq / hkv * max_q <= 2^30 rows per KV head; on the 256-row kernel
+ *   (more than 192 rows per KV head) key splits x n_seq x max_q x hq < 2^31.
  */
 typedef struct ba_attn_desc {
   int32_t dtype;            /* ba_dtype of q, k and v                          */

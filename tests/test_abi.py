@@ -324,3 +324,27 @@ def test_sparse_validation(lib):
     d.cu_q = d.cu_k = FAKE
     st, msg = status_of(lib, fn, ctypes.byref(d), FAKE, 3, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == 4 and "dense" in msg
+
+
+def test_prefix_rejects_entries_beyond_32_bit_indexing(lib):
+    # The kernels number rows per KV head and, in the 256-row kernel's
+    # epilogue, (split, row, head) entries with 32-bit integers; shapes beyond
+    # either are refused on the host (nothing is enqueued).
+    def desc(n_seq, hq, hkv, max_q):
+        d = lib_mod.AttnDesc()
+        d.dtype, d.n_seq, d.hq, d.hkv, d.d, d.max_q, d.max_k = 0, n_seq, hq, hkv, 128, max_q, 64
+        d.q = d.k = d.v = FAKE
+        for i, s in enumerate((max_q * hq * 128, hq * 128, 128)):
+            d.q_stride[i] = s
+        for i, s in enumerate((hkv * 64 * 128, 128, 64 * 128)):
+            d.k_stride[i] = s
+            d.v_stride[i] = s
+        return d
+    # 1024 query heads on one KV head over 3,000,000 rows: 3.07e9 rows per KV head
+    d = desc(1, 1024, 1, 3_000_000)
+    st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), FAKE, FAKE, FAKE, 1 << 62, None)
+    assert st == 4 and "rows per KV head" in msg, (st, msg)
+    # 4 sequences x 600,000 rows x 1024 heads = 2.46e9 entries (38.4e6 rows per KV head)
+    d = desc(4, 1024, 16, 600_000)
+    st, msg = status_of(lib, lib.ba_prefix_attn, ctypes.byref(d), FAKE, FAKE, FAKE, 1 << 62, None)
+    assert st == 4 and "entries" in msg, (st, msg)
