@@ -629,11 +629,13 @@ def test_split_attn(dtype, shape):
 
 GATED_SHAPES = [
     # (B, hq, hkv, d, lp, nb): few rows (two key-waves, split-KV), 128-row
-    # tiles (GQA), the alternating 256-row kernel, d = 64
+    # tiles (GQA), the alternating 256-row kernel, d = 64 (few rows and the
+    # 256-row kernel)
     (2, 8, 8, 128, 512, 32),
     (2, 8, 2, 128, 600, 32),
     (2, 4, 1, 128, 700, 80),
     (2, 4, 4, 64, 300, 20),
+    (2, 4, 1, 64, 500, 60),
 ]
 
 
