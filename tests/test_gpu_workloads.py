@@ -195,6 +195,14 @@ def test_workload_long_prefix():
     assert rec >= sched.B * sched.hq
 
 
+def test_workload_gqa_long_prefix():
+    # The long-context axis at the GQA shape: one sequence's 32 query heads
+    # on 8 KV heads over a 512k-token prefix (the 256-row kernel with many
+    # key splits per (sequence, KV head), and their combine), three steps.
+    sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=3, seed=9, lp=524288, B=1, steps=3)
+    assert rec >= sched.B * sched.hq
+
+
 def test_workload_gqa_cumulative_gate():
     # The GQA long-context schedule (Poisson(3) rewritten rows per step, tau
     # 8) gated on the positions updated since the last refresh: the
