@@ -54,6 +54,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "ba_internal.h"
 #include "gate_body.h"
@@ -1129,17 +1130,18 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
     pp_item<D, NS, GATE>(p0, wg, p0.decision != nullptr && p0.mode != kBlock, ready_r, smem);
 }
 
-// Compute units of the current device (looked up once per device).
+// Compute units of the current device (looked up once per device; threads
+// that race on the first lookup store the same value).
 int device_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // One entry of the combine: where it lives and what its first memory round
