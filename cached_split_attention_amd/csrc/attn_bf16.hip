@@ -703,9 +703,6 @@ __device__ __forceinline__ void bf16_item(const AttnParams& p, const int wg, uns
   static_assert(ST >= 2 && ST <= 4, "ring depth");
   constexpr int STAGE_B = 2 * TILE_B;
   constexpr int XSLOT = (DB * 16 + 2) * 64;      // floats per key-wave exchange slot
-  constexpr int SMEM_X = (KW > 1) ? (KW - 1) * RW * XSLOT * 4 : 0;
-  constexpr int SMEM_R = ST * STAGE_B;
-  constexpr int SMEM = SMEM_R > SMEM_X ? SMEM_R : SMEM_X;
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
   bool gated = p.decision != nullptr && p.mode != kBlock;
@@ -951,11 +948,25 @@ __device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool 
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
       (qvar ? (int64_t)(itm.qbase + i) * p.qs1 : (int64_t)b * p.qs0 + (int64_t)qi * p.qs1) +
       (int64_t)h * p.qs2;
-  bf16x8 qf[KS];
+  // The wave's 32 Q rows go to LDS first, through the ring's stages 2 and 3
+  // (free until tile 2 is issued), by DMA instructions that each copy RPI
+  // whole rows: a lane-per-row register load would touch 32 rows' cache
+  // lines per instruction.  Each row's 16-byte chunks are XOR-placed by row,
+  // so the operand reads below (chunk 2 ks + hf of row lr) hit distinct
+  // banks.  A wave reads back only the rows it copied itself.
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  const int q_lds_off = 2 * STAGE_B + w * (64 * D);
+  if (active) {
+    const uint64_t qa = reinterpret_cast<uint64_t>(qrow);
+    const int qlo = (int)(unsigned)qa, qhi = (int)(unsigned)(qa >> 32), qv = rvalid ? 1 : 0;
+    const int slot = lane & (CH - 1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = rvalid ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf) : u32x4{0, 0, 0, 0};
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
+    for (int j = 0; j < 32 / RPI; ++j) {
+      const int rr = RPI * j + lane / CH;
+      const uint64_t a = (uint64_t)(unsigned)__shfl(qlo, rr) | ((uint64_t)(unsigned)__shfl(qhi, rr) << 32);
+      if (__shfl(qv, rr))
+        dma16(reinterpret_cast<const uint16_t*>(a) + 8 * (slot ^ (rr & (CH - 1))), smem_base + q_lds_off + j * 1024);
+    }
   }
 
   const uint16_t* kptr = static_cast<const uint16_t*>(p.k) +
@@ -1002,6 +1013,16 @@ __device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool 
   for (int t = 0; t < LOOK; ++t)
     if (t < n) issue_tile(t);
   wait_vmem_all();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // (orders the LDS reads below after the copies)
+  bf16x8 qf[KS];
+  {
+    const unsigned char* qw = smem + q_lds_off + lr * (2 * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 16 * ((2 * ks + hf) ^ (lr & (CH - 1))));
+      qf[ks] = __builtin_bit_cast(bf16x8, rvalid ? x : u32x4{0, 0, 0, 0});
+    }
+  }
   if (grp) even_barrier(0);
   if (grp) phase_barrier<63>(); else even_barrier(0);
   if (active && n > 0) score_mfma<D, MB>(s, smem, off, qf);
