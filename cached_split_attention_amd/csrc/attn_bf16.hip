@@ -1421,7 +1421,8 @@ hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, const GateParam
 //      matrix cores set the pace
 Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
   (void)d;
-  if (prefix && rows_per_kv_head > 192) return Bf16Plan{3, 256, 64, 1};
+  // (an in-block problem with many keys is as MFMA-bound as a prefix pass)
+  if (rows_per_kv_head > 192 && (prefix || max_k > 512)) return Bf16Plan{3, 256, 64, 1};
   if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64, 2};
   if (rows_per_kv_head <= 32 && max_k <= 64 && !prefix) return Bf16Plan{2, 32, 32, 8};
   return Bf16Plan{1, 64, 64, 2};

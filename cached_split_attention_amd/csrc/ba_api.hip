@@ -571,6 +571,8 @@ ba_status ba_block_attn(const ba_attn_desc* desc, const float* a_cache, const fl
   if (desc->dtype == BA_F32) return hip_status(ba::launch_attn_f32(p, desc->d, stream), "block attention (f32)");
   const int rows = sh.group * desc->max_q;
   const ba::Bf16Plan bf = ba::plan_bf16(desc->d, rows, desc->max_k, false);
+  if (bf.variant == 3 && (int64_t)desc->n_seq * desc->max_q * desc->hq > 0x7fffffffLL)
+    return fail(BA_ERR_UNSUPPORTED, "too many (row, head) entries");   // (32-bit entry indexes)
   p.row_tiles = (rows + bf.rows_per_wg - 1) / bf.rows_per_wg;
   if ((int64_t)p.row_tiles * desc->n_seq * desc->hkv > 0x7fffff00LL)
     return fail(BA_ERR_UNSUPPORTED, "too many workgroups");

@@ -1138,7 +1138,32 @@ def test_prefix_attn_bshd_layout(dtype):
 @pytest.mark.parametrize("shape", DENSE_SHAPES)
 def test_block_attn_fused_merge(dtype, shape):
     B, hq, hkv, d, lp, nb = shape
-    s = _dense_inputs(dtype, B, hq, hkv, d, 4, nb, seed=hash(shape) % 997)
+    _check_block_attn(dtype, B, hq, hkv, d, nb, seed=hash(shape) % 997)
+
+
+# Blocks of more than 192 rows per KV head and more than 512 keys (the
+# alternating 256-row kernel): GQA with a ragged row tile and key tile, a
+# video-like pair of heads (1560 rows and keys: 6 full row tiles, a 24-row
+# tail, 24 full key tiles and a 24-key tail), d = 64 with two sequences.
+BIG_BLOCK_SHAPES = [
+    (1, 4, 1, 128, 600),
+    (1, 2, 2, 128, 1560),
+    (2, 2, 1, 64, 530),
+]
+
+
+@pytest.mark.parametrize("shape", BIG_BLOCK_SHAPES)
+def test_block_attn_many_rows_and_keys(shape):
+    B, hq, hkv, d, nb = shape
+    _check_block_attn("bf16", B, hq, hkv, d, nb, seed=nb)
+
+
+def _check_block_attn(dtype, B, hq, hkv, d, nb, seed):
+    # A_in/L_in against the in-block oracle, A_full/L_full against its merge
+    # with a random cache (some cached rows empty: L = -inf); a call without
+    # A_in/L_in gives the same A_full bit for bit, and one without the cache
+    # the same A_in/L_in.
+    s = _dense_inputs(dtype, B, hq, hkv, d, 4, nb, seed=seed)
     want_a, want_l = _oracle_block(s)
     r = np.random.default_rng(5)
     rows = B * nb
@@ -1162,6 +1187,11 @@ def test_block_attn_fused_merge(dtype, shape):
     ba.ba_block_attn(q, k, v, a_cache=dev_f32(ac), l_cache=dev_f32(lc), a_full=af)
     torch.cuda.synchronize()
     assert torch.equal(af, outs[2])
+    # no cache: the in-block part alone
+    ai, li = torch.zeros(rows, hq, d, device=DEV), torch.zeros(rows, hq, device=DEV)
+    ba.ba_block_attn(q, k, v, a_in=ai, l_in=li)
+    torch.cuda.synchronize()
+    assert torch.equal(ai, outs[0]) and torch.equal(li, outs[1])
 
 
 def test_block_attn_guard_bands():
