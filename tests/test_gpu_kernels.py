@@ -1284,6 +1284,58 @@ def test_varlen_attention(d):
     assert torch.all(a_full[tot:] == 3.0) and torch.all(a_out[tot:] == 3.0)
 
 
+def test_varlen_gqa_256_row_kernel():
+    # Packed (thd) query rows of a GQA batch with more than 192 rows per KV
+    # head, so the prefix part and (with more than 512 block keys) the
+    # in-block part run on the alternating 256-row kernel with packed Q and
+    # packed K/V: blocks of 530, 0 and 201 positions, prefixes of 300, 50 and
+    # 700 keys, 8 query heads on 2 KV heads.
+    rng = np.random.default_rng(77)
+    hq, hkv, d = 8, 2, 128
+    g = hq // hkv
+    nq = np.array([530, 0, 201])
+    lp = np.array([300, 50, 700])
+    n, nl = int(nq.sum()), int(lp.sum())
+    scale = 1.0 / math.sqrt(d)
+
+    def draw(*shape):
+        return round_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+    q, kb, vb = draw(n, hq, d), draw(n, hkv, d), draw(n, hkv, d)
+    kp, vp = draw(nl, hkv, d), draw(nl, hkv, d)
+    cq = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lp)]).astype(np.int32)
+    want = {nm: np.zeros((n, hq, d)) for nm in ("a_out", "a_in", "a_full")}
+    want.update({nm: np.zeros((n, hq)) for nm in ("l_out", "l_in", "l_full")})
+    f = lambda x: oracle.to_f64(x, "bf16")
+    for b in range(nq.size):
+        r = slice(cq[b], cq[b + 1])
+        for h in range(hq):
+            qq = f(q[r, h])
+            ao, lo = oracle.attention(qq, f(kp[ck[b]:ck[b + 1], h // g]), f(vp[ck[b]:ck[b + 1], h // g]), scale)
+            ai, li = oracle.attention(qq, f(kb[r, h // g]), f(vb[r, h // g]), scale)
+            af, lf = oracle.merge(ao, lo, ai, li)
+            for nm, x in (("a_out", ao), ("l_out", lo), ("a_in", ai), ("l_in", li), ("a_full", af), ("l_full", lf)):
+                want[nm][r, h] = x
+    cu_q, cu_kp = torch.from_numpy(cq).to(DEV), torch.from_numpy(ck).to(DEV)
+    kw = dict(q_layout="thd", cu_q=cu_q, max_q=int(nq.max()))
+    pk = dict(kv_layout="thd", cu_k=cu_kp, max_k=int(lp.max()))
+    qd = dev_bits(q)
+    out = {nm: torch.full((n, hq, d), 3.0, device=DEV) for nm in ("a_out", "a_in", "a_full")}
+    out.update({nm: torch.full((n, hq), 3.0, device=DEV) for nm in ("l_out", "l_in", "l_full")})
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(qd, dev_bits(kp), dev_bits(vp), **pk, **kw)), device=DEV,
+                     dtype=torch.uint8)
+    ba.ba_prefix_attn(qd, dev_bits(kp), dev_bits(vp), out["a_out"], out["l_out"], ws, **pk, **kw)
+    ba.ba_block_attn(qd, dev_bits(kb), dev_bits(vb), a_cache=out["a_out"], l_cache=out["l_out"], a_in=out["a_in"],
+                     l_in=out["l_in"], a_full=out["a_full"], l_full=out["l_full"], kv_layout="thd", cu_k=cu_q,
+                     max_k=int(nq.max()), **kw)
+    torch.cuda.synchronize()
+    for nm in ("a_out", "a_in", "a_full"):
+        check_a(host(out[nm]), want[nm], nm)
+    for nm in ("l_out", "l_in", "l_full"):
+        check_l(host(out[nm]), want[nm], nm)
+
+
 # ----------------------------------------------------------------------------
 # whole schedules through the step driver
 # ----------------------------------------------------------------------------
