@@ -120,6 +120,8 @@ __device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
 
 // As dma16, from a wave-uniform base plus a per-lane 32-bit byte offset (the
 // base is read from the first lane, so it lives in scalar registers).
+// NT: the load is marked nontemporal (data read once).
+template <bool NT = false>
 __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane(lds_base);
   // (readfirstlane returns int: each half goes through unsigned, so the low
@@ -128,7 +130,10 @@ __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsign
   const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
   const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
   const uint64_t su = lo | (hi << 32);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "s"(base) : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(su), "s"(base) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "s"(base) : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight,
@@ -172,8 +177,13 @@ __device__ __forceinline__ int swz(int row) {
 // l%CPR, which holds source chunk (l%CPR) ^ swz(row).  A full tile is fetched
 // from the tile's scalar base plus fixed per-lane byte offsets; the tail tile
 // clamps keys past the range to the last valid key (finite data; their scores
-// are masked).
-template <int D, int NW, int KTILE>
+// are masked).  With STREAM and `once` (a single row tile per (sequence, KV
+// head), so each tile is read by one work item only) the full-tile loads
+// are marked nontemporal: the stream then does not displace lines that are read again
+// (LLaDA-like step 10.6 -> 10.1 us, multi-branch varlen step 139 -> 133-134
+// us).  With several row tiles each tile is read once per row tile and the
+// L2 serves the repeats (the video-like pass is 2 % slower with the mark).
+template <int D, int NW, int KTILE, bool STREAM = false>
 struct TileDma {
   static constexpr int ROWB = D * 2;
   static constexpr int CPR = D / 8;
@@ -190,10 +200,12 @@ struct TileDma {
   int ke, w, l_row, l_slot;
   bool fast;
   unsigned koffs[BPW], voffs[BPW];
+  bool once;
 
   __device__ __forceinline__ TileDma(const uint16_t* kp, const uint16_t* vp, int64_t ks, int64_t vs, int kend,
-                                     int wave, int lane)
-      : kptr(kp), vptr(vp), ks1(ks), vs1(vs), ke(kend), w(wave), l_row(lane / CPR), l_slot(lane % CPR) {
+                                     int wave, int lane, bool read_once = false)
+      : kptr(kp), vptr(vp), ks1(ks), vs1(vs), ke(kend), w(wave), l_row(lane / CPR), l_slot(lane % CPR),
+        once(STREAM && read_once) {
     fast = (int64_t)KTILE * (ks1 > vs1 ? ks1 : vs1) * 2 < (1LL << 31);
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
@@ -208,11 +220,20 @@ struct TileDma {
     if (fast && t0 + KTILE <= ke) {
       const uint16_t* kt = kptr + (int64_t)t0 * ks1;
       const uint16_t* vt = vptr + (int64_t)t0 * vs1;
+      if (STREAM && once) {
 #pragma unroll
-      for (int u = 0; u < BPW; ++u) {
-        const int blk = w * BPW + u;
-        dma16_s(kt, koffs[u], kdst + blk * 1024);
-        dma16_s(vt, voffs[u], vdst + blk * 1024);
+        for (int u = 0; u < BPW; ++u) {
+          const int blk = w * BPW + u;
+          dma16_s<true>(kt, koffs[u], kdst + blk * 1024);
+          dma16_s<true>(vt, voffs[u], vdst + blk * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+          const int blk = w * BPW + u;
+          dma16_s(kt, koffs[u], kdst + blk * 1024);
+          dma16_s(vt, voffs[u], vdst + blk * 1024);
+        }
       }
     } else {
 #pragma unroll
@@ -695,7 +716,10 @@ template <int D, int RW, int KW, int KT, int ST, bool GATE>
 __device__ __forceinline__ void bf16_item(const AttnParams& p, const int wg, unsigned char* smem) {
   constexpr int NW = RW * KW;
   constexpr int KTILE = KW * KT;                 // keys per iteration tile
-  using Dma = TileDma<D, NW, KTILE>;
+  // (nontemporal K/V streams where each tile is read once; the 256-row
+  // kernel, bound by its matrix cores, keeps cached loads: the mark measured
+  // 0.3 % slower on the GQA schedule there)
+  using Dma = TileDma<D, NW, KTILE, true>;
   constexpr int TILE_B = Dma::TILE_B;            // bytes of one K (or V) tile
   constexpr int KS = D / 16;                     // MFMA k-steps over head dim
   constexpr int DB = D / 32;                     // 32-dim output blocks
@@ -751,7 +775,7 @@ __device__ __forceinline__ void bf16_item(const AttnParams& p, const int wg, uns
   // key-block list mode: tiles are the listed blocks (KTILE == kBlockKeys)
   const bool listed = p.kblocks != nullptr;
   const int entry = load_block_entry(p, itm, lane);
-  const Dma dma(kptr, vptr, p.ks1, p.vs1, listed ? itm.nk : ke, w, lane);
+  const Dma dma(kptr, vptr, p.ks1, p.vs1, listed ? itm.nk : ke, w, lane, p.row_tiles == 1);
   auto issue_tile = [&](int t0, int st) {
     const unsigned kdst = smem_base + st * STAGE_B;
     dma.issue(t0, kdst, kdst + TILE_B);
