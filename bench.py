@@ -578,6 +578,72 @@ def run_sparse(args, s, q, kps, vps):
 KL_ROWS, KL_VOCAB = 252, 126464   # the varlen batch's block positions; a vocabulary size chosen here
 
 
+def run_yardstick(args, s, q, kps, vps):
+    """Same-box yardstick: torch's fused attention (scaled_dot_product_attention,
+    flash backend forced, so nothing falls back to unfused products) on the
+    prefix-pass shape of this workload, next to the library's own prefix pass
+    over the same rotated copies.  The query heads of one KV head are packed as
+    one head of G*Nb rows, which is the same arithmetic; the output is checked
+    against the library's A_out."""
+    import torch
+    import cached_split_attention_amd as ba
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    dev = q[1].device
+    B, hq, hkv, d, nb = s.B, s.hq, s.hkv, s.d, s.nb
+    g = hq // hkv
+    qp = q[1].view(B, nb, hkv, g, d).permute(0, 2, 3, 1, 4).reshape(1, B * hkv, g * nb, d).contiguous()
+    kq = [k.view(1, B * hkv, s.lp, d) for k in kps]
+    vq = [v.view(1, B * hkv, s.lp, d) for v in vps]
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q[1], kps[0], vps[0], scale=s.scale)), device=dev,
+                     dtype=torch.uint8)
+    a = torch.empty(B * nb, hq, d, device=dev)
+    l = torch.empty(B * nb, hq, device=dev)
+    n = max(6, 2 * len(kps))
+
+    def timed(fn):
+        # warm-up of about 0.3 s, so that the clocks have settled
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for i in range(len(kps)):
+                fn(i)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i % len(kps))
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    out = {"yardstick": args.workload, "shape": {"heads": B * hkv, "rows": g * nb, "keys": s.lp, "d": d}}
+    def ours_pass(i):
+        ba.ba_prefix_attn(q[1], kps[i], vps[i], a, l, ws, scale=s.scale)
+
+    ours_before = timed(ours_pass)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            res = {}
+            sd = timed(lambda i: res.__setitem__(0, torch.nn.functional.scaled_dot_product_attention(
+                qp, kq[i], vq[i], scale=s.scale)))
+            o = torch.nn.functional.scaled_dot_product_attention(qp, kq[0], vq[0], scale=s.scale)
+        ours = (ours_before + timed(ours_pass)) / 2   # before and after, against clock drift
+        out["ours_prefix_pass_us"] = round(ours, 2)
+        ba.ba_prefix_attn(q[1], kps[0], vps[0], a, l, ws, scale=s.scale)
+        mine = a.view(B, nb, hkv, g, d).permute(0, 2, 3, 1, 4).reshape(1, B * hkv, g * nb, d)
+        torch.cuda.synchronize()
+        out["torch_sdpa_flash_us"] = round(sd, 2)
+        out["torch_rocm_fa_library"] = str(torch.backends.cuda.preferred_rocm_fa_library())
+        out["speedup"] = round(sd / ours, 2)
+        out["max_abs_diff_vs_a_out"] = float((o.float() - mine).abs().max().item())
+        flops = 4.0 * d * nb * s.lp * hq * B
+        out["tflops"] = {"ours": round(flops / ours / 1e6, 1), "torch_sdpa_flash": round(flops / sd / 1e6, 1)}
+    except Exception as ex:   # no flash kernel for this shape or build
+        out["ours_prefix_pass_us"] = round(ours_before, 2)
+        out["torch_sdpa_flash_us"] = None
+        out["error"] = f"{type(ex).__name__}: {str(ex)[:200]}"
+    print(json.dumps(out), flush=True)
+
+
 def run_kl(args):
     """The lock criterion on its own: KL of each token's posterior from the
     previous step's over a 126464-entry vocabulary, for the 252 block
@@ -686,6 +752,9 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: only the prefix pass, eagerly, over the rotated copies, "
                          "then a plain device copy of known size (the counters' scale reference)")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="time torch's fused attention (flash backend) on the prefix-pass shape beside the "
+                         "library's prefix pass, instead of the block schedule (dense workloads)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
@@ -729,6 +798,9 @@ def main():
     v = [to_dev(x) for x in s.v]
     if args.probe:
         probe(args, s, q, kps, vps)
+        return
+    if args.yardstick:
+        run_yardstick(args, s, q, kps, vps)
         return
     if args.sparse is not None:
         run_sparse(args, s, q, kps, vps)
