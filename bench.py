@@ -908,7 +908,9 @@ def main():
                          "A_full/L_full written)",
                "us": round(ib_us, 2), "algorithmic_flops": ib_flops, "algorithmic_bytes": ib_bytes,
                "tflops": round(ib_flops / (ib_us * 1e-6) / 1e12, 2),
-               "frac_mfma_bf16": round(ib_flops / (ib_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               # (against the roof its arithmetic intensity reaches first: HBM for a
+               # short block, the matrix cores for a long one)
+               "roofline": roofline_of(ib_bytes, ib_flops, ib_us)[0],
                "gbs": round(ib_bytes / (ib_us * 1e-6) / 1e9, 1),
                "timing": f"{n_ib} calls in one graph, 4 replays, HIP events on the launching stream"}
 
