@@ -47,13 +47,14 @@ KL_SOURCES = ["cached_split_attention_amd/csrc/kl.hip"]
 # algorithmic work (what the method itself reads, writes and computes)
 # ----------------------------------------------------------------------------
 
-def step_work(s, dec, esize=2):
+def step_work(s, dec, esize=2, mask=False):
     """Algorithmic (bytes, flops, prefix_bytes, prefix_flops) of one
     denoising step of schedule s with decision matrix dec [B, Hq] (1 = reuse),
     or, for the partial refresh, per-row marks dec [B, Nb] (1 = row current).
     Prefix: K/V of every KV head with a recomputed query head (partial: of
     every sequence with a recomputed row), the recomputed Q rows, their
-    A_out/L_out written.  Every step: gate inputs, block Q, K, V, the cache
+    A_out/L_out written.  Every step: gate inputs (the update mask, with
+    mask), block Q, K, V, the cache
     read by the merge, A_full/L_full written."""
     B, hq, hkv, d, lp, nb = s.B, s.hq, s.hkv, s.d, s.lp, s.nb
     g = hq // hkv
@@ -68,7 +69,9 @@ def step_work(s, dec, esize=2):
         kv_heads = int(rec.reshape(B, hkv, g).any(axis=2).sum())
         p_bytes = kv_heads * lp * d * esize * 2 + n_rec * nb * d * esize + n_rec * nb * (d + 1) * 4
         p_flops = 4 * d * nb * lp * n_rec
-    if s.gate in ("count", "count_cum"):
+    if s.gate in ("count", "count_cum") and mask:
+        gate_bytes = B * nb   # the caller's update mask
+    elif s.gate in ("count", "count_cum"):
         gate_bytes = 2 * B * nb * (hq + 2 * hkv) * d * esize
     else:
         gate_bytes = 2 * B * nb * hq * d * esize
@@ -752,6 +755,9 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: only the prefix pass, eagerly, over the rotated copies, "
                          "then a plain device copy of known size (the counters' scale reference)")
+    ap.add_argument("--update-mask", action="store_true",
+                    help="count gates: feed the gate the generator's record of the rewritten positions (the "
+                         "update mask a sampler holds) instead of comparing the block rows")
     ap.add_argument("--yardstick", action="store_true",
                     help="time torch's fused attention (flash backend) on the prefix-pass shape beside the "
                          "library's prefix pass, instead of the block schedule (dense workloads)")
@@ -810,15 +816,20 @@ def main():
     stream = torch.cuda.current_stream()
 
     # untimed eager pass: record the (deterministic) decision pattern
+    masks = None
+    if args.update_mask:
+        if s.gate not in ("count", "count_cum"):
+            raise SystemExit("--update-mask needs a count gate")
+        masks = [None] + [torch.from_numpy(s.rewritten[t]).to(dev) for t in range(1, s.steps + 1)]
     attn.start_block(kps[0], vps[0])
     decisions = [None]
     for t in range(1, s.steps + 1):
-        attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+        attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1], upd_mask=None if masks is None else masks[t])
         decisions.append(attn.decision.cpu().numpy().copy())
         if attn.waits_given_up():
             raise RuntimeError(f"step {t}: a prefix workgroup gave up waiting for its gate")
     final_out = (attn.a_full.cpu().double().numpy().copy(), attn.l_full.cpu().double().numpy().copy())
-    work = [step_work(s, decisions[t]) for t in range(1, s.steps + 1)]
+    work = [step_work(s, decisions[t], mask=masks is not None) for t in range(1, s.steps + 1)]
     blk_bytes = sum(w[0] for w in work)
     blk_flops = sum(w[1] for w in work)
     rec_steps = [t for t in range(1, s.steps + 1) if (decisions[t] == 0).any()]
@@ -826,13 +837,14 @@ def main():
 
     progress(f"eager pass done, {len(rec_steps)} recompute steps")
     # one graph per prefix copy: the whole block schedule
-    graphs = [attn.capture_block(q, k, v, kps[i], vps[i]) for i in range(n_copies)]
+    graphs = [attn.capture_block(q, k, v, kps[i], vps[i], masks=masks) for i in range(n_copies)]
     # single-step graphs for per-step latency
-    g_rec = attn.capture(q, k, v, [1], new_block=True, kp=kps[0], vp=vps[0])
+    g_rec = attn.capture(q, k, v, [1], new_block=True, kp=kps[0], vp=vps[0], masks=masks)
     # a reuse step repeated in place (same inputs, same decision, same
     # outputs) REUSE_REPS times in one graph, so the per-graph launch cost is
     # spread as it is over a block schedule
-    g_reuse = attn.capture(q, k, v, [reuse_steps[0]] * REUSE_REPS, new_block=False) if reuse_steps else None
+    g_reuse = (attn.capture(q, k, v, [reuse_steps[0]] * REUSE_REPS, new_block=False, masks=masks)
+               if reuse_steps else None)
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -929,7 +941,8 @@ def main():
         "data": "synthetic, seeded (workloads.preset), resident in HBM",
         "config": {"workload": f"{args.workload}: B={s.B} Hq={s.hq} Hkv={s.hkv} d={s.d} "
                                f"prefix={s.lp} block={s.nb} steps/block={s.steps} gate={s.gate}"
-                               f" tau={s.tau} gamma={s.gamma}",
+                               f" tau={s.tau} gamma={s.gamma}"
+                               + (" gate_input=update_mask" if masks is not None else ""),
                    "bench_step": "one block schedule (every denoising step), replayed as a HIP graph",
                    "prefix_kv_copies": n_copies},
         "tflops": round(blk_flops / (ms_per_step * 1e-3) / 1e12, 4),

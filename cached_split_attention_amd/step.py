@@ -102,11 +102,15 @@ class CachedBlockAttention:
                 n = ba_gated_split_attn_gate_workspace(self.mode, q, q_prev, **kw)
             self._gws = torch.zeros(max(n, 1), device=q.device, dtype=torch.uint8)
 
-    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None):
+    def step(self, q, k, v, q_prev, k_prev, v_prev, stream=None, upd_mask=None):
         """Run one step; returns (a_full, l_full) views of the output buffers.
 
         With no valid cache the gate still runs (it reports M), but the prefix
-        part is not gated by it: everything recomputes."""
+        part is not gated by it: everything recomputes.  upd_mask (uint8
+        [B, Nb], count gates only): the caller's own record of the positions it
+        updated since the previous step, counted instead of comparing rows."""
+        if upd_mask is not None and self.mode not in (BA_GATE_COUNT, BA_GATE_COUNT_CUM):
+            raise ValueError("an update mask feeds the count gates only")
         self._workspaces(q, k, v, q_prev, k_prev, v_prev)
         main = stream if stream is not None else torch.cuda.current_stream()
         if self.mode == BA_GATE_ROWS:
@@ -117,7 +121,7 @@ class CachedBlockAttention:
         ba_gated_split_attn(self.mode, q_prev, self.kp, self.vp, k, v, self.a_out, self.l_out, self.a_in,
                             self.l_in, self.a_full, self.l_full, self._ws, q=q, decision=self.decision,
                             gate_workspace=self._gws, k_prev=k_prev if count else None,
-                            v_prev=v_prev if count else None, tau=self.tau, gamma=self.gamma,
+                            v_prev=v_prev if count else None, upd_mask=upd_mask, tau=self.tau, gamma=self.gamma,
                             cache_valid=self.cache_valid, m_count=self.m_count if count else None,
                             cos=None if count else self.cos,
                             since_refresh=getattr(self, "since_refresh", None), kv_layout=self.kv_layout,
@@ -142,13 +146,14 @@ class CachedBlockAttention:
         ba_block_attn(q, k, v, a_cache=self.a_out, l_cache=self.l_out, a_in=self.a_in, l_in=self.l_in,
                       a_full=self.a_full, l_full=self.l_full, scale=self.scale, stream=stream)
 
-    def capture(self, q, k, v, steps, new_block=True, kp=None, vp=None):
+    def capture(self, q, k, v, steps, new_block=True, kp=None, vp=None, masks=None):
         """Capture the given steps of a block's schedule as one HIP graph.
 
         q, k, v: sequences of block tensors, index 0 = the block before step 1,
         index t = the block at step t.  With new_block the graph starts a new
         block (no valid cache); otherwise the cache is taken as valid.
         Replaying the graph re-runs those steps on the same buffers.
+        masks: optional per-step update masks (masks[t] for step t), as in step().
         Workspaces are allocated before capture and no memset is recorded
         (the gate's tickets are cleared by its own workgroups and its ready
         counts by the combine pass), so replays need no re-initialisation.
@@ -165,11 +170,12 @@ class CachedBlockAttention:
                 self.cache_valid = not new_block
                 for t in steps:
                     self.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1],
-                              stream=torch.cuda.current_stream())
+                              stream=torch.cuda.current_stream(),
+                              upd_mask=None if masks is None else masks[t])
         torch.cuda.current_stream().wait_stream(side)
         self.cache_valid = True
         return graph
 
-    def capture_block(self, q, k, v, kp=None, vp=None):
+    def capture_block(self, q, k, v, kp=None, vp=None, masks=None):
         """One block's whole schedule (steps 1 .. len(q)-1) as one graph."""
-        return self.capture(q, k, v, range(1, len(q)), new_block=True, kp=kp, vp=vp)
+        return self.capture(q, k, v, range(1, len(q)), new_block=True, kp=kp, vp=vp, masks=masks)

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from workloads import preset
-from tests.gpu_util import check_a, check_l, dev_bits, dev_in, host
+from tests.gpu_util import DEV, check_a, check_l, dev_bits, dev_in, host
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +80,12 @@ def _check_whole_heads(sched, t, pairs, last, attn, cache, name):
 
 
 def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=False, seed=0, whole=None,
-                          **overrides):
+                          use_mask=False, **overrides):
     """whole(sched, gates) -> {step: [(b, h), ...]}: (sequence, head) pairs
-    whose every row is checked at that step, besides the sampled rows."""
+    whose every row is checked at that step, besides the sampled rows.
+    use_mask: the count gate is fed the generator's record of rewritten
+    positions (a caller's update mask) instead of comparing rows; decisions
+    and M must still equal the oracle's row comparison."""
     sched = preset(name, **overrides)
     say(f"[{name}] B={sched.B} Hq={sched.hq} Hkv={sched.hkv} d={sched.d} Lp={sched.lp} Nb={sched.nb} "
         f"steps={sched.steps} gate={sched.gate}")
@@ -92,6 +95,8 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
         margins = [np.abs(gates[t]["cos"] - sched.gamma).min() for t in range(2, sched.steps + 1)]
         assert min(margins) > 1e-6, f"seed gives a near-tie cosine ({min(margins):.2e})"
     q, k, v = _to_dev(sched)
+    masks = ([None] + [torch.from_numpy(sched.rewritten[t]).to(DEV) for t in range(1, sched.steps + 1)]
+             if use_mask else None)
     kp, vp = dev_in(sched.kp, sched.dtype), dev_in(sched.vp, sched.dtype)
     attn = ba.CachedBlockAttention(kp, vp, nb=sched.nb, hq=sched.hq, gate=sched.gate, tau=sched.tau,
                                    gamma=sched.gamma, scale=sched.scale)
@@ -103,7 +108,7 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
     if use_graph:
         # step-by-step graphs, as replayed by the benchmark's per-step legs,
         # and the whole-block graph it times
-        g = attn.capture_block(q, k, v)
+        g = attn.capture_block(q, k, v, masks=masks)
         g.replay()
         torch.cuda.synchronize()
         say(f"[{name}] whole-block graph replayed")
@@ -111,7 +116,8 @@ def _run_schedule_checked(name, rows_per_step=8, full_rows=False, use_graph=Fals
         attn.start_block()
     recomputes = 0
     for t in range(1, sched.steps + 1):
-        af, lf = attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1])
+        af, lf = attn.step(q[t], k[t], v[t], q[t - 1], k[t - 1], v[t - 1],
+                           upd_mask=None if masks is None else masks[t])
         torch.cuda.synchronize()
         dec = attn.decision.cpu().numpy()
         assert np.array_equal(dec, gates[t]["decision"]), f"[{name}] step {t}: decisions differ"
@@ -169,6 +175,13 @@ def _gqa_whole(sched, gates):
 def test_workload_gqa_long_context():
     sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=6, use_graph=False, seed=3, whole=_gqa_whole)
     assert rec > sched.B * sched.hq  # gated recomputes beyond the first step
+
+
+def test_workload_gqa_update_mask():
+    # the same schedule with the count gate reading the caller's update mask
+    # (the fused launch's mask path), whole-block graph included
+    sched, rec = _run_schedule_checked("c3_gqa_long", rows_per_step=4, use_graph=True, seed=5, use_mask=True)
+    assert rec > sched.B * sched.hq
 
 
 def _video_whole(sched, gates):

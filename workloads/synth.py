@@ -75,7 +75,9 @@ class BlockSchedule:
     q[t], k[t], v[t] hold the block rows seen by step t (t = 1..steps);
     index 0 is the block as drawn before step 1.  touched[t, b] is how many
     block positions of sequence b the generator rewrote going from t-1 to t
-    (the generator's own record, kept apart from any comparison of rows).
+    (the generator's own record, kept apart from any comparison of rows);
+    rewritten[t, b, p] is 1 where position p was one of them (the update mask
+    a sampler knows without comparing rows).
     """
 
     name: str
@@ -98,6 +100,7 @@ class BlockSchedule:
     k: list = field(default_factory=list)
     v: list = field(default_factory=list)
     touched: np.ndarray = None
+    rewritten: np.ndarray = None
     sigma: np.ndarray = None     # cosine schedules: per (step, head) noise level
 
     @property
@@ -141,6 +144,7 @@ def make_block_schedule(*, name="custom", dtype="bf16", B=1, hq=4, hkv=4, d=128,
     sch.k.append(k0)
     sch.v.append(v0)
     touched = np.zeros((steps + 1, B), dtype=np.int32)
+    rewritten = np.zeros((steps + 1, B, nb), dtype=np.uint8)
     masked = [list(range(nb)) for _ in range(B)]
     sigma = np.zeros((steps + 1, hq), dtype=np.float64) if schedule == "qnoise" else None
 
@@ -157,6 +161,7 @@ def make_block_schedule(*, name="custom", dtype="bf16", B=1, hq=4, hkv=4, d=128,
             sch.k.append(kpv)
             sch.v.append(vpv)
             touched[t, :] = nb
+            rewritten[t] = 1
             continue
         if schedule == "none":
             sch.q.append(qp)
@@ -185,6 +190,7 @@ def make_block_schedule(*, name="custom", dtype="bf16", B=1, hq=4, hkv=4, d=128,
                 raise ValueError(f"unknown schedule {schedule!r}")
             pos = np.sort(np.asarray(pos, dtype=np.int64))
             touched[t, b] = pos.size
+            rewritten[t, b, pos] = 1
             if pos.size:
                 nq[b, pos] = _draw(rng, (pos.size, hq, d), dtype, std)
                 nk[b, pos] = _draw(rng, (pos.size, hkv, d), dtype, std)
@@ -193,6 +199,7 @@ def make_block_schedule(*, name="custom", dtype="bf16", B=1, hq=4, hkv=4, d=128,
         sch.k.append(nk)
         sch.v.append(nv)
     sch.touched = touched
+    sch.rewritten = rewritten
     sch.sigma = sigma
     return sch
 
