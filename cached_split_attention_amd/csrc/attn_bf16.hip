@@ -1442,8 +1442,8 @@ hipError_t launch_pp(const AttnParams& p0, const AttnParams* p1, const GateParam
 //      2 WG per CU)
 //   1:  64 rows (2 row-waves x 2 key-waves of 32) x 64 keys (2 WG per CU);
 //       also used for fewer rows: the streaming, not the MFMA, sets the pace
-//   2:  32 rows x 32 keys, one wave (8 KB LDS at d=128): small in-block
-//       problems, where latency dominates
+//   2:  32 rows x 32 keys, one wave (32 KB LDS at d=128: 5 WG per CU): in-block
+//       problems over short blocks, where latency dominates
 //   3: 256 rows (two alternating groups of 4 waves) x 64 keys, 4-stage ring
 //      (128 KB LDS at d=128: 1 WG per CU): many rows per KV head, where the
 //      matrix cores set the pace
@@ -1451,8 +1451,12 @@ Bf16Plan plan_bf16(int d, int rows_per_kv_head, int max_k, bool prefix) {
   (void)d;
   // (an in-block problem with many keys is as MFMA-bound as a prefix pass)
   if (rows_per_kv_head > 192 && (prefix || max_k > 512)) return Bf16Plan{3, 256, 64, 1};
+  // an in-block call over a short block is latency-bound whatever its row
+  // count: one-wave workgroups of 32 rows give the most of them (the GQA
+  // long-context in-block call, 256 rows per KV head over 64 keys: 12.6-12.9
+  // -> 11.1-11.2 us against the 128-row workgroups)
+  if (max_k <= 64 && !prefix) return Bf16Plan{2, 32, 32, 5};
   if (rows_per_kv_head > 64) return Bf16Plan{0, 128, 64, 2};
-  if (rows_per_kv_head <= 32 && max_k <= 64 && !prefix) return Bf16Plan{2, 32, 32, 8};
   return Bf16Plan{1, 64, 64, 2};
 }
 
