@@ -534,8 +534,8 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
   }
 }
 
-// Epilogue of the 256-row kernel for the modes without the fused merge
-// (split partial, final prefix result, A_in/L_in): the wave's normalised
+// Epilogue of the 256-row kernel (split partial, final prefix result,
+// A_in/L_in, and the in-block result with the fused merge): the wave's normalised
 // 32 x D block goes through its own LDS region (the ring is free once every
 // tile is consumed), so that each global store writes whole rows (D floats
 // contiguous) instead of a 32-byte piece of each of 32 rows.  In LDS, row rr
@@ -543,8 +543,11 @@ __device__ __forceinline__ void write_result(const AttnParams& p, int mode, bool
 // row-owning writes and the chunk-owning reads both spread over the banks.
 // The stores are nontemporal: the rows are read back by the next pass, not
 // by this one (the GQA reuse step measured 20.9 -> 19.8 us with them).
+// The fused merge reads the cached rows chunk by chunk the same way and
+// writes A_full as whole rows (the video-like in-block call with the merge:
+// 55.6-56.1 -> 50.4-50.8 us against the direct 32-byte stores).
 // Every wave of the workgroup must call it (it starts with a barrier).
-template <int D>
+template <int D, bool MERGE>
 __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mode, bool writer, const RowOut& ro,
                                                     const f32x16 (&o)[D / 32], float m_run, float l_tot,
                                                     unsigned char* wave_lds) {
@@ -563,8 +566,25 @@ __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mod
   float* l_base = partial ? p.ws_l : p.l;
   const int64_t ent = partial ? (int64_t)ro.split * n_entries + ro.prow * p.hq + ro.h : ro.orow * p.hq + ro.h;
   const int my_ent = writer ? (int)ent : -1;
+  constexpr int NI = 32 / RPI;       // wave-wide stores per 32 rows
+  const int cc = lane % CH;          // the chunk this lane stores
 
   wait_vmem_all();
+  // In-block result with the fused merge: the cached prefix rows this lane
+  // merges (the chunks it stores) are loaded first, all together, so their
+  // latency hides behind the barrier and the staging below.
+  const bool merge = MERGE && mode == kBlock && p.a_cache != nullptr;
+  float lc[NI];
+  f32x4 cv[NI];
+  if constexpr (MERGE) if (merge) {
+#pragma unroll
+    for (int s = 0; s < NI; ++s) {
+      const int e = __shfl(my_ent, RPI * s + lane / CH);
+      lc[s] = e >= 0 ? p.l_cache[e] : -INFINITY;
+      cv[s] = (e >= 0 && p.a_full) ? *reinterpret_cast<const f32x4*>(p.a_cache + (int64_t)e * D + 4 * cc)
+                                   : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
   __syncthreads();   // every wave is done with the ring
   f32x4* rowp = reinterpret_cast<f32x4*>(wave_lds + lr * (D * 4));
 #pragma unroll
@@ -576,9 +596,8 @@ __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mod
                                         o[db][4 * j + 3] * inv};
     }
   if (a_base) {
-    const int cc = lane % CH;
 #pragma unroll
-    for (int s = 0; s < 32 / RPI; ++s) {
+    for (int s = 0; s < NI; ++s) {
       const int rr = RPI * s + lane / CH;
       const int e = __shfl(my_ent, rr);
       const f32x4 val = reinterpret_cast<const f32x4*>(wave_lds + rr * (D * 4))[cc ^ (rr & (CH - 1))];
@@ -586,6 +605,25 @@ __device__ __forceinline__ void write_result_staged(const AttnParams& p, int mod
     }
   }
   if (l_base && writer && hf == 0) l_base[ent] = L;
+  if constexpr (MERGE) if (merge) {
+    // the merge equation, cache first and in-block part second, from the
+    // normalised A_in as staged (the same arithmetic as the direct epilogue)
+#pragma unroll
+    for (int s = 0; s < NI; ++s) {
+      const int rr = RPI * s + lane / CH;
+      const int e = __shfl(my_ent, rr);
+      const float li = __shfl(L, rr);
+      const MergeWeights mw = merge_weights(lc[s], li);
+      if (e >= 0 && p.a_full) {
+        const f32x4 val = reinterpret_cast<const f32x4*>(wave_lds + rr * (D * 4))[cc ^ (rr & (CH - 1))];
+        f32x4 af;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) af[k] = merge_elem(mw, cv[s][k], val[k]);
+        __builtin_nontemporal_store(af, reinterpret_cast<f32x4*>(p.a_full + (int64_t)e * D + 4 * cc));
+      }
+      if (e >= 0 && p.l_full && cc == 0) p.l_full[e] = mw.l;
+    }
+  }
 }
 
 // Work item of a workgroup covering ROWS query rows: (sequence, KV head,
@@ -931,7 +969,7 @@ attn_bf16_kernel(const AttnParams p0, const AttnParams p1, int grid0, const Gate
 // decisions (with p.ready: read through the gate's ready words; ready_r >= 0
 // is the gate result already read).  Every wave of the workgroup returns
 // from it together.
-template <int D, int NS, bool GATE>
+template <int D, int NS, bool GATE, bool MERGE = false>
 __device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool gated, const int ready_r,
                                         unsigned char* smem) {
   constexpr int NW = 8, ROWS = 256, KT = 64;
@@ -1073,10 +1111,14 @@ __device__ __forceinline__ void pp_item(const AttnParams& p, const int wg, bool 
   if (gated) writer = writer && !reused(p, b, h);
   const RowOut ro{qvar ? (int64_t)(itm.qbase + i) : (int64_t)b * p.max_q + qi, (int64_t)b * p.max_q + i, h, hf,
                   itm.split};
-  if (itm.mode == kBlock && p.a_cache)
+  // (the fused merge belongs to the stand-alone in-block call, whose launch
+  // is the plain one-part kernel; the other launches keep its code out)
+  if constexpr (MERGE)
+    write_result_staged<D, true>(p, itm.mode, writer, ro, o, m_run, l_tot, smem + w * (32 * D * 4));
+  else if (itm.mode == kBlock && p.a_cache)
     write_result<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, nullptr, 0.0f);
   else
-    write_result_staged<D>(p, itm.mode, writer, ro, o, m_run, l_tot, smem + w * (32 * D * 4));
+    write_result_staged<D, false>(p, itm.mode, writer, ro, o, m_run, l_tot, smem + w * (32 * D * 4));
 }
 
 // Alternating-phase kernel: 8 waves, 256 query rows, 64-key tiles in an
@@ -1172,7 +1214,7 @@ attn_pp_kernel(const AttnParams p0, const AttnParams p1, int grid0, const GatePa
   if (second)
     pp_item<D, NS, GATE>(p1, wg, p1.decision != nullptr && p1.mode != kBlock, ready_r, smem);
   else
-    pp_item<D, NS, GATE>(p0, wg, p0.decision != nullptr && p0.mode != kBlock, ready_r, smem);
+    pp_item<D, NS, GATE, !DUAL && !GATE>(p0, wg, p0.decision != nullptr && p0.mode != kBlock, ready_r, smem);
 }
 
 // Compute units of the current device (looked up once per device; threads
