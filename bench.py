@@ -283,6 +283,30 @@ def probe(args, s, q, kps, vps):
     print(json.dumps({"probe": args.workload, "prefix_passes": 2 * len(kps),
                       "copy_bytes_each": COPY_PROBE_BYTES, "copies": 4}), flush=True)
 
+def probe_inblock(args, s, q, k, v, kps, vps):
+    """Launches for per-dispatch counters of the in-block part alone: the
+    cache is filled by one prefix pass, then 4 ba_block_attn calls over the
+    last step's block with the fused merge (A_in/L_in and A_full/L_full
+    written), eagerly."""
+    import torch
+    import cached_split_attention_amd as ba
+    dev = q[1].device
+    ws = torch.zeros(max(1, ba.ba_prefix_attn_workspace(q[1], kps[0], vps[0], scale=s.scale)), device=dev,
+                     dtype=torch.uint8)
+    rows = s.B * s.nb
+    a_out = torch.empty(rows, s.hq, s.d, device=dev)
+    l_out = torch.empty(rows, s.hq, device=dev)
+    ba.ba_prefix_attn(q[s.steps], kps[0], vps[0], a_out, l_out, ws, scale=s.scale)
+    outs = [torch.empty_like(a_out), torch.empty_like(l_out), torch.empty_like(a_out), torch.empty_like(l_out)]
+    torch.cuda.synchronize()
+    for _ in range(4):
+        ba.ba_block_attn(q[s.steps], k[s.steps], v[s.steps], a_cache=a_out, l_cache=l_out, a_in=outs[0],
+                         l_in=outs[1], a_full=outs[2], l_full=outs[3], scale=s.scale)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_inblock": args.workload, "calls": 4,
+                      "algorithmic_flops_per_call": 4 * s.d * s.nb * s.nb * s.B * s.hq}), flush=True)
+
+
 def roofline_of(p_bytes, p_flops, us):
     """The roof a pass of this arithmetic intensity reaches first, and the
     fraction of it achieved in `us` microseconds."""
@@ -758,6 +782,9 @@ def main():
     ap.add_argument("--update-mask", action="store_true",
                     help="count gates: feed the gate the generator's record of the rewritten positions (the "
                          "update mask a sampler holds) instead of comparing the block rows")
+    ap.add_argument("--probe-inblock", action="store_true",
+                    help="counter-collection mode for the in-block part alone: 4 eager ba_block_attn calls "
+                         "with the cache merge (after one prefix pass fills the cache)")
     ap.add_argument("--yardstick", action="store_true",
                     help="time torch's fused attention (flash backend) on the prefix-pass shape beside the "
                          "library's prefix pass, instead of the block schedule (dense workloads)")
@@ -807,6 +834,9 @@ def main():
         return
     if args.yardstick:
         run_yardstick(args, s, q, kps, vps)
+        return
+    if args.probe_inblock:
+        probe_inblock(args, s, q, k, v, kps, vps)
         return
     if args.sparse is not None:
         run_sparse(args, s, q, kps, vps)
